@@ -1,0 +1,205 @@
+"""Python binding of libcpattn (blockwise zigzag-ring varlen attention on
+MI355X).  Argument marshalling only: every step of the path runs in the HIP
+kernels of libcpattn.so; torch supplies device memory and the stream.
+
+The functions carry the names of the C entry points in include/cpattn.h.
+Tensors are THD torch tensors ([tokens, heads, head_dim], head_dim
+contiguous); LSE / delta arrays are fp32 [heads, tokens]; fp32 accumulators
+are dense [tokens, heads, head_dim].  A non-zero status raises CpattnError.
+
+There is no fallback: if libcpattn.so is missing or fails to load, importing
+this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcpattn.so")
+
+CAUSAL, BIDIR, TF_BLOCK = 0, 1, 2
+F32, BF16 = 0, 1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+
+EXPORTS = (
+    "cpattn_version", "cpattn_status_string", "cpattn_partition_index", "cpattn_partition",
+    "cpattn_unpartition", "cpattn_count_pairs", "cpattn_workspace_size", "cpattn_workspace_status",
+    "cpattn_fwd_step", "cpattn_merge", "cpattn_bwd_preprocess", "cpattn_bwd_step",
+)
+
+
+class CpattnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int), ("tokens", ctypes.c_int64),
+                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("stride_token", ctypes.c_int64), ("stride_head", ctypes.c_int64)]
+
+
+class Step(ctypes.Structure):
+    _fields_ = [("cp", ctypes.c_int32), ("rank", ctypes.c_int32), ("step", ctypes.c_int32),
+                ("tf_chunk_tokens", ctypes.c_int32), ("tf_num_chunks", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libcpattn.so not built at {LIB_PATH}; run python -m context_attention_varlen_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    TP = ctypes.POINTER(Tensor)
+    SP = ctypes.POINTER(Step)
+    sig = {
+        "cpattn_version": (ctypes.c_char_p, []),
+        "cpattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "cpattn_partition_index": (ctypes.c_int, [P, I32, I32, I32, P, P]),
+        "cpattn_partition": (ctypes.c_int, [TP, TP, P, I32, I32, I32, P]),
+        "cpattn_unpartition": (ctypes.c_int, [TP, TP, P, I32, I32, I32, P]),
+        "cpattn_count_pairs": (I64, [P, I32, ctypes.c_int, SP]),
+        "cpattn_workspace_size": (S, [I64, I64, I32]),
+        "cpattn_workspace_status": (ctypes.c_int, [P, P, ctypes.POINTER(ctypes.c_int)]),
+        "cpattn_fwd_step": (ctypes.c_int, [TP, TP, TP, P, P, I32, ctypes.c_int, SP, F, TP, P, P, S, P]),
+        "cpattn_merge": (ctypes.c_int, [P, P, TP, P, P]),
+        "cpattn_bwd_preprocess": (ctypes.c_int, [P, TP, P, P]),
+        "cpattn_bwd_step": (ctypes.c_int, [TP, TP, TP, TP, P, P, P, P, I32, ctypes.c_int, SP, F,
+                                           P, P, P, P, S, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def status_string(status: int) -> str:
+    return _lib.cpattn_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != OK:
+        raise CpattnError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _tensor(t) -> Tensor:
+    if t.dim() != 3:
+        raise ValueError("THD tensors are [tokens, heads, head_dim]")
+    if t.stride(2) != 1:
+        raise ValueError("head_dim must be contiguous")
+    return Tensor(t.data_ptr(), _dtype_code(t), t.shape[0], t.shape[1], t.shape[2], t.stride(0), t.stride(1))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_step(cp, rank, step, tf_chunk_tokens=0, tf_num_chunks=0) -> Step:
+    return Step(cp, rank, step, tf_chunk_tokens, tf_num_chunks)
+
+
+# ---------------------------------------------------------------------------
+# entry points (names as in include/cpattn.h)
+# ---------------------------------------------------------------------------
+def cpattn_version() -> str:
+    return _lib.cpattn_version().decode()
+
+
+def cpattn_partition_index(cu_seqlens_global, cp: int, rank: int, with_map: bool = True):
+    """Host index plan: (cu_seqlens_local int32, local_to_global int64 or None)."""
+    cu = np.ascontiguousarray(cu_seqlens_global, dtype=np.int32)
+    nseq = len(cu) - 1
+    cu_l = np.zeros(nseq + 1, np.int32)
+    l2g = np.zeros(int(cu[-1]) // cp if nseq >= 0 else 0, np.int64) if with_map else None
+    st = _lib.cpattn_partition_index(cu.ctypes.data, nseq, cp, rank, cu_l.ctypes.data,
+                                     l2g.ctypes.data if l2g is not None else None)
+    _check(st, "cpattn_partition_index")
+    return cu_l, l2g
+
+
+def cpattn_partition(src_global, dst_local, cu_seqlens_global_dev, num_seqs, cp, rank, stream=None):
+    st = _lib.cpattn_partition(ctypes.byref(_tensor(src_global)), ctypes.byref(_tensor(dst_local)),
+                               _ptr(cu_seqlens_global_dev), num_seqs, cp, rank, _stream(stream))
+    _check(st, "cpattn_partition")
+
+
+def cpattn_unpartition(src_local, dst_global, cu_seqlens_global_dev, num_seqs, cp, rank, stream=None):
+    st = _lib.cpattn_unpartition(ctypes.byref(_tensor(src_local)), ctypes.byref(_tensor(dst_global)),
+                                 _ptr(cu_seqlens_global_dev), num_seqs, cp, rank, _stream(stream))
+    _check(st, "cpattn_unpartition")
+
+
+def cpattn_count_pairs(cu_seqlens_global, mask_mode, step: Step) -> int:
+    cu = np.ascontiguousarray(cu_seqlens_global, dtype=np.int32)
+    n = _lib.cpattn_count_pairs(cu.ctypes.data, len(cu) - 1, mask_mode, ctypes.byref(step))
+    if n < 0:
+        raise CpattnError(ERR_INVALID_ARG, "cpattn_count_pairs")
+    return int(n)
+
+
+def cpattn_workspace_size(tokens_q, tokens_k, num_seqs) -> int:
+    return int(_lib.cpattn_workspace_size(tokens_q, tokens_k, num_seqs))
+
+
+def cpattn_workspace_status(workspace, stream=None) -> int:
+    out = ctypes.c_int(-1)
+    _check(_lib.cpattn_workspace_status(_ptr(workspace), _stream(stream), ctypes.byref(out)),
+           "cpattn_workspace_status")
+    return out.value
+
+
+def cpattn_fwd_step(q, k, v, cu_seqlens_q_dev, cu_seqlens_k_dev, num_seqs, mask_mode, step: Step,
+                    softmax_scale, out_partial, lse_partial, workspace, stream=None):
+    st = _lib.cpattn_fwd_step(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)), ctypes.byref(_tensor(v)),
+                              _ptr(cu_seqlens_q_dev), _ptr(cu_seqlens_k_dev), num_seqs, mask_mode,
+                              ctypes.byref(step), float(softmax_scale), ctypes.byref(_tensor(out_partial)),
+                              _ptr(lse_partial), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "cpattn_fwd_step")
+
+
+def cpattn_merge(out, lse, out_partial, lse_partial, stream=None):
+    st = _lib.cpattn_merge(_ptr(out), _ptr(lse), ctypes.byref(_tensor(out_partial)), _ptr(lse_partial),
+                           _stream(stream))
+    _check(st, "cpattn_merge")
+
+
+def cpattn_bwd_preprocess(out, dout, delta, stream=None):
+    st = _lib.cpattn_bwd_preprocess(_ptr(out), ctypes.byref(_tensor(dout)), _ptr(delta), _stream(stream))
+    _check(st, "cpattn_bwd_preprocess")
+
+
+def cpattn_bwd_step(q, k, v, dout, lse, delta, cu_seqlens_q_dev, cu_seqlens_k_dev, num_seqs, mask_mode,
+                    step: Step, softmax_scale, dq_accum, dk_accum, dv_accum, workspace, stream=None):
+    st = _lib.cpattn_bwd_step(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)), ctypes.byref(_tensor(v)),
+                              ctypes.byref(_tensor(dout)), _ptr(lse), _ptr(delta), _ptr(cu_seqlens_q_dev),
+                              _ptr(cu_seqlens_k_dev), num_seqs, mask_mode, ctypes.byref(step),
+                              float(softmax_scale), _ptr(dq_accum), _ptr(dk_accum), _ptr(dv_accum),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "cpattn_bwd_step")

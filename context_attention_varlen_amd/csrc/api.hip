@@ -1,0 +1,326 @@
+// libcpattn C ABI: argument validation and dispatch.  Every entry point
+// checks its arguments before anything is enqueued; no C++ exception leaves
+// this file.
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "common.h"
+
+#define CPATTN_API extern "C" __attribute__((visibility("default")))
+
+using namespace cpattn;
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_size(cpattn_dtype t) { return t == CPATTN_BF16 ? 2 : 4; }
+
+// A THD view the kernels can use: 16-byte aligned rows, head_dim 64 or 128.
+cpattn_status check_tensor(const cpattn_tensor* t, bool need_data = true) {
+  if (!t) return CPATTN_ERR_INVALID_ARG;
+  if (t->dtype != CPATTN_F32 && t->dtype != CPATTN_BF16) return CPATTN_ERR_UNSUPPORTED;
+  if (t->tokens < 0 || t->tokens >= kMaxRows || t->heads <= 0) return CPATTN_ERR_INVALID_ARG;
+  if (t->head_dim != 64 && t->head_dim != 128) return CPATTN_ERR_UNSUPPORTED;
+  if (need_data && t->tokens > 0 && (!t->data || !aligned16(t->data))) return CPATTN_ERR_INVALID_ARG;
+  if (t->stride_token % 8 || t->stride_head % 8) return CPATTN_ERR_INVALID_ARG;
+  // views whose (token, head) rows overlap are rejected: writes through
+  // them would race
+  if (t->heads > 1 && t->stride_head < t->head_dim) return CPATTN_ERR_INVALID_ARG;
+  if (t->tokens > 1 && t->stride_token < (int64_t)(t->heads - 1) * t->stride_head + t->head_dim)
+    return CPATTN_ERR_INVALID_ARG;
+  return CPATTN_OK;
+}
+
+cpattn_status check_step(const cpattn_step* s, cpattn_mask_mode mode) {
+  if (!s) return CPATTN_ERR_INVALID_ARG;
+  if (s->cp < 1 || s->rank < 0 || s->rank >= s->cp || s->step < 0 || s->step >= s->cp)
+    return CPATTN_ERR_INVALID_ARG;
+  if (mode != CPATTN_MASK_CAUSAL && mode != CPATTN_MASK_BIDIR && mode != CPATTN_MASK_TF_BLOCK)
+    return CPATTN_ERR_INVALID_ARG;
+  if (mode == CPATTN_MASK_TF_BLOCK) {
+    if (s->tf_chunk_tokens <= 0 || s->tf_num_chunks <= 0) return CPATTN_ERR_INVALID_ARG;
+    if ((int64_t)s->tf_chunk_tokens * s->tf_num_chunks * 2 >= kMaxRows) return CPATTN_ERR_INVALID_ARG;
+    if (s->cp != 1) return CPATTN_ERR_UNSUPPORTED;
+  }
+  return CPATTN_OK;
+}
+
+int src_rank(const cpattn_step* s) { return ((s->rank - s->step) % s->cp + s->cp) % s->cp; }
+
+cpattn_status hip_status(hipError_t e) { return e == hipSuccess ? CPATTN_OK : CPATTN_ERR_HIP; }
+
+// Host closed form: pairs (p, k), p in [a, a+C), k in [b, b+Cb), k <= p.
+int64_t causal_block_pairs(int64_t a, int64_t C, int64_t b, int64_t Cb) {
+  if (C <= 0 || Cb <= 0) return 0;
+  auto F = [Cb](int64_t n) -> int64_t {  // sum_{y=1..n} min(y, Cb), 0 for n <= 0
+    if (n <= 0) return 0;
+    if (n <= Cb) return n * (n + 1) / 2;
+    return Cb * (Cb + 1) / 2 + (n - Cb) * Cb;
+  };
+  const int64_t x0 = a - b + 1, x1 = a - b + C;
+  return F(x1) - F(x0 - 1);
+}
+
+// Shared set-up of the scheduler arguments.
+SchedArgs sched_args(void* ws, int64_t ws_bytes_needed, const int32_t* cu_p, const int32_t* cu_s, int nseq,
+                     int64_t tok_p, int64_t tok_s, const cpattn_step* st, int rank_p, int rank_s,
+                     bool primary_is_q, cpattn_mask_mode mode, int tile_p, int tile_s, int cost_mult,
+                     int64_t max_items, const WsLayout& L) {
+  (void)ws_bytes_needed;
+  SchedArgs a;
+  a.cu_p = cu_p;
+  a.cu_s = cu_s;
+  a.nseq = nseq;
+  a.tokens_p = tok_p;
+  a.tokens_s = tok_s;
+  a.cp = st->cp;
+  a.rank_p = rank_p;
+  a.rank_s = rank_s;
+  a.primary_is_q = primary_is_q ? 1 : 0;
+  a.mask = (int)mode;
+  a.tf_b = mode == CPATTN_MASK_TF_BLOCK ? st->tf_chunk_tokens : 1;
+  a.tf_n = mode == CPATTN_MASK_TF_BLOCK ? st->tf_num_chunks : 1;
+  a.tile_p = tile_p;
+  a.tile_s = tile_s;
+  a.cost_mult = cost_mult;
+  a.max_items = (int32_t)max_items;
+  char* base = (char*)ws;
+  a.hdr = (WsHeader*)(base + L.hdr);
+  a.items = (WorkItem*)(base + L.items);
+  a.order = (int32_t*)(base + L.order);
+  a.seq_base = (int32_t*)(base + L.seq_base);
+  return a;
+}
+
+}  // namespace
+
+CPATTN_API const char* cpattn_version(void) { return "cpattn 0.1 (gfx950)"; }
+
+CPATTN_API const char* cpattn_status_string(cpattn_status s) {
+  switch (s) {
+    case CPATTN_OK: return "ok";
+    case CPATTN_ERR_INVALID_ARG: return "invalid argument";
+    case CPATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CPATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case CPATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+CPATTN_API cpattn_status cpattn_partition_index(const int32_t* cu_g, int32_t nseq, int32_t cp, int32_t rank,
+                                                int32_t* cu_l, int64_t* l2g) {
+  if (!cu_g || !cu_l || nseq < 0 || cp < 1 || rank < 0 || rank >= cp) return CPATTN_ERR_INVALID_ARG;
+  if (cu_g[0] != 0) return CPATTN_ERR_INVALID_ARG;
+  for (int b = 0; b < nseq; ++b) {
+    const int64_t len = (int64_t)cu_g[b + 1] - cu_g[b];
+    if (len < 0) return CPATTN_ERR_INVALID_ARG;
+    if (cp > 1 && len % (2 * cp)) return CPATTN_ERR_INVALID_ARG;
+  }
+  cu_l[0] = 0;
+  int64_t t = 0;
+  for (int b = 0; b < nseq; ++b) {
+    const int64_t g0 = cu_g[b], len = (int64_t)cu_g[b + 1] - g0;
+    if (cp == 1) {
+      if (l2g)
+        for (int64_t o = 0; o < len; ++o) l2g[t + o] = g0 + o;
+      t += len;
+    } else {
+      const int64_t C = len / (2 * cp);
+      const int64_t chunks[2] = {rank, 2 * cp - 1 - rank};
+      for (int h = 0; h < 2; ++h)
+        for (int64_t o = 0; o < C; ++o) {
+          if (l2g) l2g[t] = g0 + chunks[h] * C + o;
+          ++t;
+        }
+    }
+    cu_l[b + 1] = (int32_t)t;
+  }
+  return CPATTN_OK;
+}
+
+static cpattn_status partition_common(const cpattn_tensor* src, cpattn_tensor* dst, const int32_t* cu_dev,
+                                      int32_t nseq, int32_t cp, int32_t rank, void* stream, bool scatter) {
+  cpattn_status st;
+  if ((st = check_tensor(src)) != CPATTN_OK) return st;
+  if ((st = check_tensor(dst)) != CPATTN_OK) return st;
+  if (!cu_dev || nseq < 0 || cp < 1 || rank < 0 || rank >= cp) return CPATTN_ERR_INVALID_ARG;
+  if (src->dtype != dst->dtype || src->heads != dst->heads || src->head_dim != dst->head_dim)
+    return CPATTN_ERR_INVALID_ARG;
+  const cpattn_tensor* glob = scatter ? dst : src;
+  const cpattn_tensor* loc = scatter ? src : dst;
+  if (loc->tokens < glob->tokens / cp) return CPATTN_ERR_INVALID_ARG;
+  const int es = elem_size(src->dtype);
+  PartArgs a;
+  a.src = (const char*)src->data;
+  a.dst = (char*)dst->data;
+  a.src_st = src->stride_token * es;
+  a.src_sh = src->stride_head * es;
+  a.dst_st = dst->stride_token * es;
+  a.dst_sh = dst->stride_head * es;
+  a.cu = cu_dev;
+  a.nseq = nseq;
+  a.local_tokens = glob->tokens / cp;
+  a.global_tokens = glob->tokens;
+  a.heads = src->heads;
+  a.row_bytes = src->head_dim * es;
+  a.cp = cp;
+  a.rank = rank;
+  a.scatter = scatter ? 1 : 0;
+  return hip_status(launch_partition(a, (hipStream_t)stream));
+}
+
+CPATTN_API cpattn_status cpattn_partition(const cpattn_tensor* src_global, cpattn_tensor* dst_local,
+                                          const int32_t* cu_dev, int32_t nseq, int32_t cp, int32_t rank,
+                                          void* stream) {
+  return partition_common(src_global, dst_local, cu_dev, nseq, cp, rank, stream, false);
+}
+
+CPATTN_API cpattn_status cpattn_unpartition(const cpattn_tensor* src_local, cpattn_tensor* dst_global,
+                                            const int32_t* cu_dev, int32_t nseq, int32_t cp, int32_t rank,
+                                            void* stream) {
+  return partition_common(src_local, dst_global, cu_dev, nseq, cp, rank, stream, true);
+}
+
+CPATTN_API int64_t cpattn_count_pairs(const int32_t* cu_g, int32_t nseq, cpattn_mask_mode mode,
+                                      const cpattn_step* st) {
+  if (!cu_g || nseq < 0 || check_step(st, mode) != CPATTN_OK || cu_g[0] != 0) return -1;
+  const int cp = st->cp, r = st->rank, j = src_rank(st);
+  int64_t total = 0;
+  for (int b = 0; b < nseq; ++b) {
+    const int64_t L = (int64_t)cu_g[b + 1] - cu_g[b];
+    if (L < 0 || (cp > 1 && L % (2 * cp))) return -1;
+    if (mode == CPATTN_MASK_TF_BLOCK) {
+      const int64_t B = st->tf_chunk_tokens, N = st->tf_num_chunks;
+      if (L != 2 * B * N) return -1;
+      total += N * (N + 1) * B * B;
+      continue;
+    }
+    if (cp == 1) {
+      total += mode == CPATTN_MASK_BIDIR ? L * L : causal_block_pairs(0, L, 0, L);
+      continue;
+    }
+    const int64_t C = L / (2 * cp);
+    const int64_t qc[2] = {r, 2 * cp - 1 - r}, kc[2] = {j, 2 * cp - 1 - j};
+    for (int x = 0; x < 2; ++x)
+      for (int y = 0; y < 2; ++y)
+        total += mode == CPATTN_MASK_BIDIR ? C * C : causal_block_pairs(qc[x] * C, C, kc[y] * C, C);
+  }
+  return total;
+}
+
+CPATTN_API size_t cpattn_workspace_size(int64_t tokens_q, int64_t tokens_k, int32_t nseq) {
+  if (tokens_q < 0 || tokens_k < 0 || nseq < 0) return 0;
+  return ws_layout(tokens_q, tokens_k, nseq).total;
+}
+
+CPATTN_API cpattn_status cpattn_workspace_status(const void* ws, void* stream, cpattn_status* out) {
+  if (!ws || !out) return CPATTN_ERR_INVALID_ARG;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return CPATTN_ERR_HIP;
+  int32_t v = 0;
+  if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return CPATTN_ERR_HIP;
+  *out = (cpattn_status)v;
+  return CPATTN_OK;
+}
+
+CPATTN_API cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                         const int32_t* cu_q, const int32_t* cu_k, int32_t nseq,
+                                         cpattn_mask_mode mode, const cpattn_step* step, float scale,
+                                         cpattn_tensor* out, float* lse, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  cpattn_status st;
+  if ((st = check_tensor(q)) || (st = check_tensor(k)) || (st = check_tensor(v)) || (st = check_tensor(out)))
+    return st;
+  if ((st = check_step(step, mode)) != CPATTN_OK) return st;
+  if (q->dtype != k->dtype || q->dtype != v->dtype || q->dtype != out->dtype) return CPATTN_ERR_INVALID_ARG;
+  if (q->head_dim != k->head_dim || q->head_dim != v->head_dim || q->head_dim != out->head_dim)
+    return CPATTN_ERR_INVALID_ARG;
+  if (k->heads != v->heads || q->heads != out->heads || q->heads % k->heads) return CPATTN_ERR_INVALID_ARG;
+  if (q->tokens != out->tokens || k->tokens != v->tokens) return CPATTN_ERR_INVALID_ARG;
+  if (!cu_q || !cu_k || nseq < 0 || (!lse && q->tokens > 0) || (lse && !aligned16(lse)))
+    return CPATTN_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(q->tokens, k->tokens, nseq);
+  if (!ws || ws_bytes < L.total || !aligned16(ws)) return CPATTN_ERR_WORKSPACE;
+
+  const bool bf16 = q->dtype == CPATTN_BF16;
+  const int d = q->head_dim;
+  const int tile_p = bf16 ? 128 : 64;
+  const int64_t max_items = max_items_for(q->tokens, nseq, tile_p);
+  const SchedArgs sa = sched_args(ws, L.total, cu_q, cu_k, nseq, q->tokens, k->tokens, step, step->rank,
+                                  src_rank(step), true, mode, tile_p, 64, 1, max_items, L);
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = hip_status(launch_sched(sa, s))) != CPATTN_OK) return st;
+  if (nseq == 0 || q->tokens == 0) return CPATTN_OK;
+
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
+  FwdArgs a;
+  a.q = q->data;
+  a.k = k->data;
+  a.v = v->data;
+  a.q_st = q->stride_token; a.q_sh = q->stride_head;
+  a.k_st = k->stride_token; a.k_sh = k->stride_head;
+  a.v_st = v->stride_token; a.v_sh = v->stride_head;
+  a.out = out->data;
+  a.o_st = out->stride_token; a.o_sh = out->stride_head;
+  a.lse = lse;
+  a.tq = q->tokens;
+  a.hq = q->heads;
+  a.hkv = k->heads;
+  a.grp = q->heads / k->heads;
+  a.scale = sc;
+  a.scale_log2 = sc * 1.4426950408889634f;
+  a.mask = (int)mode;
+  a.tf_b = sa.tf_b;
+  a.tf_n = sa.tf_n;
+  a.hdr = sa.hdr;
+  a.items = sa.items;
+  a.order = sa.order;
+  return hip_status(launch_fwd(a, bf16, d, max_items, s));
+}
+
+CPATTN_API cpattn_status cpattn_merge(float* out, float* lse, const cpattn_tensor* op, const float* lsep,
+                                      void* stream) {
+  cpattn_status st;
+  if ((st = check_tensor(op)) != CPATTN_OK) return st;
+  if (op->tokens > 0 && (!out || !lse || !lsep || !aligned16(out))) return CPATTN_ERR_INVALID_ARG;
+  MergeArgs a;
+  a.out = out;
+  a.lse = lse;
+  a.op = op->data;
+  a.op_st = op->stride_token;
+  a.op_sh = op->stride_head;
+  a.lsep = lsep;
+  a.tokens = op->tokens;
+  a.heads = op->heads;
+  a.d = op->head_dim;
+  a.bf16 = op->dtype == CPATTN_BF16;
+  return hip_status(launch_merge(a, (hipStream_t)stream));
+}
+
+CPATTN_API cpattn_status cpattn_bwd_preprocess(const float* out, const cpattn_tensor* dout, float* delta,
+                                               void* stream) {
+  cpattn_status st;
+  if ((st = check_tensor(dout)) != CPATTN_OK) return st;
+  if (dout->tokens > 0 && (!out || !delta || !aligned16(out))) return CPATTN_ERR_INVALID_ARG;
+  DeltaArgs a;
+  a.out = out;
+  a.dout = dout->data;
+  a.do_st = dout->stride_token;
+  a.do_sh = dout->stride_head;
+  a.delta = delta;
+  a.tokens = dout->tokens;
+  a.heads = dout->heads;
+  a.d = dout->head_dim;
+  a.bf16 = dout->dtype == CPATTN_BF16;
+  return hip_status(launch_delta(a, (hipStream_t)stream));
+}
+
+CPATTN_API cpattn_status cpattn_bwd_step(const cpattn_tensor*, const cpattn_tensor*, const cpattn_tensor*,
+                                         const cpattn_tensor*, const float*, const float*, const int32_t*,
+                                         const int32_t*, int32_t, cpattn_mask_mode, const cpattn_step*, float,
+                                         float*, float*, float*, void*, size_t, void*) {
+  return CPATTN_ERR_UNSUPPORTED;
+}

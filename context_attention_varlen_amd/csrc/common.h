@@ -1,0 +1,184 @@
+// Internal definitions shared by the libcpattn HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cpattn.h"
+
+namespace cpattn {
+
+// ---------------------------------------------------------------------------
+// Work items built by the device-side varlen tile scheduler.
+//
+// A work item is one tile of rows on the "primary" side (query rows for the
+// forward and the dQ pass, key rows for the dK/dV pass) inside one zigzag
+// chunk of one sequence, plus up to two segments of rows on the other side
+// that hold every row the tile may attend (or be attended by).  Inside a
+// segment, rows [full_lo, full_hi) are allowed for every primary row of the
+// tile, so tiles lying inside that range need no element mask.
+// ---------------------------------------------------------------------------
+struct Segment {
+  int32_t row;      // absolute tensor row of the segment's first row
+  int32_t pos;      // in-sequence position of that row
+  int32_t n;        // rows in the segment
+  int32_t full_lo;  // [full_lo, full_hi): offsets allowed for every tile row
+  int32_t full_hi;
+};
+
+struct WorkItem {
+  int32_t seq;
+  int32_t row0;     // absolute tensor row of the tile's first primary row
+  int32_t nrows;    // primary rows in this tile
+  int32_t pos0;     // in-sequence position of the first primary row
+  int32_t cost;     // secondary tiles to visit (sum over segments)
+  int32_t nseg;
+  Segment seg[2];
+};
+static_assert(sizeof(WorkItem) == 64, "work item is one 64-byte record");
+
+// Workspace header (first 256 bytes of the workspace).
+struct WsHeader {
+  int32_t status;     // cpattn_status left by the last scheduler run
+  int32_t n_items;    // items produced
+  int32_t pad[62];
+};
+static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
+
+struct SchedArgs {
+  const int32_t* cu_p;   // cu_seqlens of the primary side (local)
+  const int32_t* cu_s;   // cu_seqlens of the secondary side (local)
+  int32_t nseq;
+  int64_t tokens_p;      // rows of the primary tensor
+  int64_t tokens_s;      // rows of the secondary tensor
+  int32_t cp;
+  int32_t rank_p;        // rank owning the primary rows
+  int32_t rank_s;        // rank owning the secondary rows
+  int32_t primary_is_q;  // 1: primary = queries, 0: primary = keys
+  int32_t mask;
+  int32_t tf_b, tf_n;
+  int32_t tile_p;        // primary tile rows
+  int32_t tile_s;        // secondary tile rows (cost unit)
+  int32_t cost_mult;     // cost multiplier (GQA group size for the dK/dV pass)
+  int32_t max_items;
+  WsHeader* hdr;
+  WorkItem* items;
+  int32_t* order;        // items sorted by cost, descending
+  int32_t* seq_base;     // [nseq + 1] first item of every sequence
+};
+
+// Workspace carve-up shared by host code.
+struct WsLayout {
+  size_t hdr, items, order, seq_base, total;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kMinTile = 64;   // smallest primary tile any kernel uses
+
+inline int64_t max_items_for(int64_t tokens, int32_t nseq, int tile) {
+  // every sequence contributes at most two chunks, each with a ragged tail
+  return (tokens + tile - 1) / tile + 2 * (int64_t)nseq + 1;
+}
+
+inline WsLayout ws_layout(int64_t tokens_q, int64_t tokens_k, int32_t nseq) {
+  int64_t tmax = tokens_q > tokens_k ? tokens_q : tokens_k;
+  int64_t mi = max_items_for(tmax, nseq, kMinTile);
+  WsLayout L;
+  L.hdr = 0;
+  L.items = 256;
+  L.order = align_up(L.items + mi * sizeof(WorkItem), 256);
+  L.seq_base = align_up(L.order + mi * sizeof(int32_t), 256);
+  L.total = align_up(L.seq_base + (nseq + 1) * sizeof(int32_t), 256);
+  return L;
+}
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh;
+  void* out;
+  int64_t o_st, o_sh;
+  float* lse;
+  int64_t tq;          // lse row stride (query tokens)
+  int hq, hkv, grp;
+  float scale;         // softmax scale
+  float scale_log2;    // scale * log2(e)
+  int mask, tf_b, tf_n;
+  const WsHeader* hdr;
+  const WorkItem* items;
+  const int32_t* order;
+};
+
+struct MergeArgs {
+  float* out;
+  float* lse;
+  const void* op;
+  int64_t op_st, op_sh;
+  const float* lsep;
+  int64_t tokens;
+  int heads;
+  int d;
+  int bf16;
+};
+
+struct DeltaArgs {
+  const float* out;
+  const void* dout;
+  int64_t do_st, do_sh;
+  float* delta;
+  int64_t tokens;
+  int heads;
+  int d;
+  int bf16;
+};
+
+struct PartArgs {
+  const char* src;
+  char* dst;
+  int64_t src_st, src_sh, dst_st, dst_sh;  // strides in bytes
+  const int32_t* cu;                        // global cu_seqlens
+  int nseq;
+  int64_t local_tokens;                     // upper bound on local rows (launch size)
+  int64_t global_tokens;                    // rows of the global tensor
+  int heads;
+  int row_bytes;                            // head_dim * element size (multiple of 16)
+  int cp, rank;
+  int scatter;                              // 0: global -> local, 1: local -> global
+};
+
+hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_delta(const DeltaArgs& a, hipStream_t stream);
+hipError_t launch_partition(const PartArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+// Position in the unsplit sequence of local row `off` of a sequence whose
+// local length is `len`, held by `rank` under the zigzag split: the local
+// rows are [chunk rank ; chunk 2cp-1-rank], each len/2 long.
+__device__ __forceinline__ int32_t zigzag_pos(int32_t off, int32_t len, int32_t cp, int32_t rank) {
+  if (cp == 1) return off;
+  int32_t c = len >> 1;
+  return off < c ? rank * c + off : (2 * cp - 1 - rank) * c + (off - c);
+}
+
+// The mask predicate on in-sequence positions (query pq, key pk).
+__device__ __forceinline__ bool mask_allowed(int mode, int32_t pq, int32_t pk, int32_t tf_b, int32_t tf_n) {
+  if (mode == CPATTN_MASK_CAUSAL) return pk <= pq;
+  if (mode == CPATTN_MASK_BIDIR) return true;
+  const int32_t span = tf_b * tf_n;
+  const bool qn = pq >= span, kn = pk >= span;
+  const int32_t cq = (qn ? pq - span : pq) / tf_b;
+  const int32_t ck = (kn ? pk - span : pk) / tf_b;
+  if (!qn) return !kn && ck <= cq;
+  return kn ? ck == cq : ck < cq;
+}
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace cpattn

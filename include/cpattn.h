@@ -1,0 +1,228 @@
+/*
+ * cpattn.h — C ABI of libcpattn: one context-parallel rank's blockwise
+ * (zigzag ring) attention over packed variable-length sequences, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  "Scaling Video Training with Parallelism" (section 2,
+ * Ring Attention paragraph) describes ring attention as blockwise attention:
+ * each device attends its local queries to one key/value block at a time
+ * while the blocks travel round the ring, and the per-block results are
+ * combined.  The LongVILA article names the zigzag variant
+ * (ZIGZAG-RINGATTN) that balances causal work across ranks.  "Speeding up
+ * Variable-Length Training with Dynamic Context Parallelism and NVIDIA
+ * Megatron Core" (section A2) fixes the input format: packed THD tensors
+ * (batch folded into the token dimension) described by cu_seqlens, with the
+ * context-parallel size carried per batch.  On one GPU the ring's K/V steps
+ * are iterated locally at their real per-rank shapes; nothing here talks to
+ * another GPU.
+ *
+ * Calling sequence for rank r of cp ranks:
+ *     cpattn_partition (Q to rank r, K/V to every source rank)
+ *     out = 0, lse = -inf
+ *     for s in 0..cp-1:
+ *         cpattn_fwd_step(step = {cp, r, s})     -> out_partial, lse_partial
+ *         cpattn_merge(out, lse, out_partial, lse_partial)
+ *     backward:
+ *         cpattn_bwd_preprocess(out, dout)       -> delta
+ *         for s in 0..cp-1: cpattn_bwd_step(step = {cp, r, s})
+ *
+ * Conventions shared by every entry point
+ *   Memory.   Every pointer named *_dev or held in a cpattn_tensor is device
+ *             memory owned by the caller; *_host pointers are host memory.
+ *             The library never allocates, frees or keeps caller memory and
+ *             keeps no per-call state.  Scratch space is the caller's
+ *             `workspace` (size from cpattn_workspace_size).
+ *   Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *             stream).  Device calls only enqueue work on it; none
+ *             synchronises, except cpattn_workspace_status which waits for
+ *             the stream.  Calls are thread-safe; calls that share one
+ *             workspace must be ordered on one stream.
+ *   Errors.   Arguments are checked before anything is launched; on failure
+ *             the call returns a non-zero status and enqueues nothing.  A
+ *             failed launch returns CPATTN_ERR_HIP.  No C++ exception
+ *             crosses this boundary.  cu_seqlens arrays in device memory are
+ *             checked on the device (non-decreasing, cu[0] = 0, within the
+ *             tensor, chunk-divisible when cp > 1); a bad array makes the
+ *             call write nothing and leaves a status code in the workspace
+ *             that cpattn_workspace_status returns.
+ *   Layout.   THD: row t of a [tokens, heads, head_dim] tensor is token t;
+ *             head_dim is contiguous; strides are in elements.  LSE and
+ *             delta arrays are fp32 [heads][tokens], contiguous.  fp32
+ *             accumulators (out, dq, dk, dv) are dense [tokens][heads][d].
+ *   Softmax.  s_ij = scale * <q_i, k_j>, natural-log LSE; scale <= 0
+ *             selects 1/sqrt(head_dim).  A query row with no allowed key in
+ *             a step gets out_partial = 0 and lse_partial = -inf.
+ *   GQA.      Hq must be a multiple of Hkv; q-head h reads kv-head
+ *             h / (Hq/Hkv) (contiguous groups).
+ *   Types.    q, k, v, dout, out_partial share one dtype: bf16 (head_dim
+ *             128 or 64, MFMA path) or fp32 (head_dim 64 or 128).
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CPATTN_OK = 0,
+    CPATTN_ERR_INVALID_ARG = 1,   /* bad pointer, size, stride, rank/step, cu_seqlens */
+    CPATTN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (dtype, head_dim, mask+cp) */
+    CPATTN_ERR_WORKSPACE = 3,     /* workspace missing or too small */
+    CPATTN_ERR_HIP = 4            /* a HIP runtime call or launch failed */
+} cpattn_status;
+
+typedef enum { CPATTN_F32 = 0, CPATTN_BF16 = 1 } cpattn_dtype;
+
+/* Masks over in-sequence positions of the unsplit sequence.
+ *   CAUSAL   key position <= query position.
+ *   BIDIR    every key of the same sequence.
+ *   TF_BLOCK teacher forcing ("Scaling Video Training with Parallelism",
+ *            section 4): each sequence is [clean history ; noisy target],
+ *            N time chunks of B tokens per stream (sequence length 2*N*B).
+ *            Clean chunk c sees clean chunks <= c; noisy chunk c sees clean
+ *            chunks < c plus its own noisy chunk.  Only with cp = 1. */
+typedef enum { CPATTN_MASK_CAUSAL = 0, CPATTN_MASK_BIDIR = 1, CPATTN_MASK_TF_BLOCK = 2 } cpattn_mask_mode;
+
+/* A THD tensor view.  data: device pointer, 16-byte aligned.  stride_token
+ * and stride_head in elements, multiples of 8 (16 bytes for bf16, 32 for
+ * fp32); the head_dim elements of one (token, head) are contiguous. */
+typedef struct {
+    void* data;
+    cpattn_dtype dtype;
+    int64_t tokens;
+    int32_t heads;
+    int32_t head_dim;
+    int64_t stride_token;
+    int64_t stride_head;
+} cpattn_tensor;
+
+/* One ring step: rank `rank` of `cp` ranks at step `step`; its K/V are the
+ * share of rank (rank - step) mod cp.  tf_chunk_tokens (B) and
+ * tf_num_chunks (N) are read only for CPATTN_MASK_TF_BLOCK. */
+typedef struct {
+    int32_t cp;
+    int32_t rank;
+    int32_t step;
+    int32_t tf_chunk_tokens;
+    int32_t tf_num_chunks;
+} cpattn_step;
+
+const char* cpattn_version(void);
+const char* cpattn_status_string(cpattn_status s);
+
+/* ---- zigzag partition -----------------------------------------------------
+ * Zigzag split (LongVILA article, ZIGZAG-RINGATTN; the chunk rule is not
+ * printed there, this is the reading that balances causal work exactly):
+ * sequence b of length L_b is cut into 2*cp chunks of C_b = L_b/(2*cp)
+ * tokens and rank r keeps chunks r and 2*cp-1-r, in that order.  The local
+ * tensor is, sequence after sequence, [chunk r ; chunk 2cp-1-r]; its
+ * cu_seqlens are the prefix sums of L_b/cp.  cp = 1 is the identity (no
+ * divisibility requirement).  Requires L_b % (2*cp) == 0 when cp > 1. */
+
+/* Host-only index plan.  cu_seqlens_global_host[num_seqs+1] (int32, cu[0]=0,
+ * non-decreasing).  Writes cu_seqlens_local_host[num_seqs+1] and, when not
+ * NULL, local_to_global_host[cu_global[num_seqs]/cp] (global row of every
+ * local row).  Bit-exact integer work; INVALID_ARG on a bad array. */
+cpattn_status cpattn_partition_index(const int32_t* cu_seqlens_global_host, int32_t num_seqs,
+                                     int32_t cp, int32_t rank,
+                                     int32_t* cu_seqlens_local_host,
+                                     int64_t* local_to_global_host);
+
+/* Device gather of rank `rank`'s share: dst_local[t] = src_global[l2g(t)]
+ * for every local row t < cu_global[num_seqs]/cp.  src and dst have equal
+ * dtype, heads and head_dim; dst->tokens >= src tokens / cp.  Copies bytes
+ * (bit-exact).  cu_seqlens_global_dev: device int32[num_seqs+1]. */
+cpattn_status cpattn_partition(const cpattn_tensor* src_global, cpattn_tensor* dst_local,
+                               const int32_t* cu_seqlens_global_dev, int32_t num_seqs,
+                               int32_t cp, int32_t rank, void* stream);
+
+/* Inverse scatter: dst_global[l2g(t)] = src_local[t].  Rows of other ranks
+ * are left untouched. */
+cpattn_status cpattn_unpartition(const cpattn_tensor* src_local, cpattn_tensor* dst_global,
+                                 const int32_t* cu_seqlens_global_dev, int32_t num_seqs,
+                                 int32_t cp, int32_t rank, void* stream);
+
+/* Exact number of allowed (query, key) pairs per head between rank `rank`'s
+ * queries and the keys it holds at ring step `step` (host-only, closed form
+ * per sequence).  This is the count behind FLOP accounting from real
+ * sequence lengths ("Speeding up Variable-Length Training ...", section A2,
+ * loss and FLOPS accounting): forward 4*d*Hq*pairs, backward 10*d*Hq*pairs.
+ * Returns -1 on invalid arguments. */
+int64_t cpattn_count_pairs(const int32_t* cu_seqlens_global_host, int32_t num_seqs,
+                           cpattn_mask_mode mask_mode, const cpattn_step* step);
+
+/* ---- workspace -------------------------------------------------------------
+ * Bytes of device workspace any call below needs for a rank with tokens_q
+ * local query rows, tokens_k local key rows and num_seqs sequences. */
+size_t cpattn_workspace_size(int64_t tokens_q, int64_t tokens_k, int32_t num_seqs);
+
+/* Waits for `stream`, then reads the device-side status the last call on
+ * this workspace left (CPATTN_OK or CPATTN_ERR_INVALID_ARG for a bad
+ * device cu_seqlens array). */
+cpattn_status cpattn_workspace_status(const void* workspace, void* stream, cpattn_status* status_out);
+
+/* ---- forward step ----------------------------------------------------------
+ * Blockwise attention of rank step->rank's local queries against the K/V
+ * share it holds at ring step step->step ("Scaling Video Training with
+ * Parallelism", section 2, Ring Attention paragraph).  Masks are applied on
+ * positions in the unsplit sequences, recovered from the zigzag rule.
+ *   q            [Tq, Hq, d]      local queries (rank step->rank)
+ *   k, v         [Tk, Hkv, d]     K/V share of rank (rank - step) mod cp
+ *   cu_seqlens_q_dev, cu_seqlens_k_dev  local int32[num_seqs+1]; for cp > 1
+ *                and for CAUSAL / TF_BLOCK the per-sequence lengths of q and k
+ *                must match (every rank's share has the same lengths).
+ *   out_partial  [Tq, Hq, d]      same dtype as q; every row of every sequence
+ *                                 is overwritten (0 for rows with no key)
+ *   lse_partial_dev  fp32 [Hq][Tq]  (-inf for rows with no key)
+ * Fully masked tiles are skipped by a device-side tile scheduler. */
+cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                              const int32_t* cu_seqlens_q_dev, const int32_t* cu_seqlens_k_dev,
+                              int32_t num_seqs, cpattn_mask_mode mask_mode, const cpattn_step* step,
+                              float softmax_scale, cpattn_tensor* out_partial, float* lse_partial_dev,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- LSE merge -------------------------------------------------------------
+ * Folds one step's partial result into the running result, in place, as the
+ * softmax over the union of two disjoint key sets:
+ *     lse' = log(exp(lse) + exp(lse_p))
+ *     out' = exp(lse - lse') * out + exp(lse_p - lse') * out_p
+ * Rows with lse_p = -inf pass through bit-exact (and are not read);
+ * running rows at -inf take the partial.
+ *   out_dev      fp32 [T][H][d] dense, running output (in/out)
+ *   lse_dev      fp32 [H][T], running LSE (in/out)
+ *   out_partial  [T, H, d] bf16 or fp32 view
+ *   lse_partial_dev fp32 [H][T] */
+cpattn_status cpattn_merge(float* out_dev, float* lse_dev, const cpattn_tensor* out_partial,
+                           const float* lse_partial_dev, void* stream);
+
+/* ---- backward --------------------------------------------------------------
+ * delta_dev[h][t] = <dout[t,h,:], out[t,h,:]> with out the final merged fp32
+ * output (dense [T][H][d]).  dout: [T, H, d] bf16 or fp32 view. */
+cpattn_status cpattn_bwd_preprocess(const float* out_dev, const cpattn_tensor* dout,
+                                    float* delta_dev, void* stream);
+
+/* One ring step of the backward, recomputing P from the saved final LSE:
+ *     P_ij = exp(scale <q_i,k_j> - lse_i),  dS_ij = P_ij (<dO_i,v_j> - delta_i)
+ *     dq_accum[i]  += scale * sum_j dS_ij k_j
+ *     dk_accum[j]  += scale * sum_i dS_ij q_i     (summed over a GQA group)
+ *     dv_accum[j]  += sum_i P_ij dO_i             (summed over a GQA group)
+ * j runs over the keys of source rank (rank - step) mod cp; dk/dv_accum are
+ * that source's buffers.  Accumulators are fp32 dense, += (caller zeroes
+ * them once).  lse_dev / delta_dev: fp32 [Hq][Tq] from the forward merge and
+ * cpattn_bwd_preprocess. */
+cpattn_status cpattn_bwd_step(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                              const cpattn_tensor* dout, const float* lse_dev, const float* delta_dev,
+                              const int32_t* cu_seqlens_q_dev, const int32_t* cu_seqlens_k_dev,
+                              int32_t num_seqs, cpattn_mask_mode mask_mode, const cpattn_step* step,
+                              float softmax_scale, float* dq_accum_dev, float* dk_accum_dev,
+                              float* dv_accum_dev, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CPATTN_H */

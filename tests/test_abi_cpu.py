@@ -1,0 +1,150 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, its host-only functions agree bit-exactly with the oracle,
+and invalid arguments are rejected before anything is launched (these calls
+never reach the GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+c = pytest.importorskip("context_attention_varlen_amd")
+
+
+def test_exports_match_header(root_dir):
+    hdr = open(os.path.join(root_dir, "include", "cpattn.h")).read()
+    declared = set(re.findall(r"\b(cpattn_[a-z_]+)\s*\(", hdr))
+    assert declared == set(c.EXPORTS)
+    lib = ctypes.CDLL(c.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in c.cpattn_version()
+    assert c.status_string(c.OK) == "ok"
+    for s in (1, 2, 3, 4):
+        assert c.status_string(s) != "ok"
+
+
+@pytest.mark.parametrize("lens,cp", [([256], 4), ([64, 0, 192, 16], 4), ([40, 24, 8], 2), ([37, 5], 1),
+                                     ([48, 16, 80, 8, 1024], 4), ([128, 64], 8)])
+def test_partition_index_matches_oracle(lens, cp):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    for r in range(cp):
+        cu_l, l2g = c.cpattn_partition_index(cu, cp, r)
+        cu_o, l2g_o, _, _ = oracle.local_rows(cu, cp, r)
+        assert np.array_equal(cu_l, cu_o)
+        assert np.array_equal(l2g, l2g_o)
+
+
+def test_partition_index_full_configs():
+    for name in ("long_video", "long_tail"):
+        w = workloads.WORKLOADS[name]
+        for r in (0, w.cp - 1):
+            cu_l, l2g = c.cpattn_partition_index(w.cu_seqlens, w.cp, r)
+            cu_o, l2g_o, _, _ = oracle.local_rows(w.cu_seqlens, w.cp, r)
+            assert np.array_equal(cu_l, cu_o) and np.array_equal(l2g, l2g_o)
+
+
+def test_partition_index_rejects_bad_input():
+    with pytest.raises(c.CpattnError):
+        c.cpattn_partition_index([0, 20], 4, 0)          # 20 % 8 != 0
+    with pytest.raises(c.CpattnError):
+        c.cpattn_partition_index([0, 16, 8], 2, 0)       # decreasing
+    with pytest.raises(c.CpattnError):
+        c.cpattn_partition_index([4, 16], 1, 0)          # cu[0] != 0
+    with pytest.raises(c.CpattnError):
+        c.cpattn_partition_index([0, 16], 2, 2)          # rank out of range
+
+
+@pytest.mark.parametrize("lens,cp,mode,tf", [
+    ([256], 4, 0, (0, 0)), ([64, 0, 192, 16], 4, 0, (0, 0)), ([40, 24, 8], 2, 1, (0, 0)),
+    ([37, 5, 100], 1, 0, (0, 0)), ([96, 160], 2, 1, (0, 0)), ([2 * 3 * 37], 1, 2, (37, 3)),
+    ([2 * 4 * 10, 2 * 4 * 10], 1, 2, (10, 4)), ([480, 32, 64], 8, 0, (0, 0))])
+def test_count_pairs_matches_oracle_brute_force(lens, cp, mode, tf):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    for r in range(cp):
+        for s in range(cp):
+            n = c.cpattn_count_pairs(cu, mode, c.make_step(cp, r, s, *tf))
+            assert n == oracle.count_pairs(cu, cp, r, s, mode, *tf)
+
+
+def test_count_pairs_configs():
+    W = workloads.WORKLOADS
+    tot = lambda w, r: sum(c.cpattn_count_pairs(w.cu_seqlens, w.mask, c.make_step(w.cp, r, s, w.tf_chunk, w.tf_num))  # noqa
+                           for s in range(w.cp))
+    assert tot(W["tiny_fp32"], 0) == 8224
+    assert tot(W["packed_varlen"], 0) == 22_395_656
+    assert tot(W["long_video"], 0) == tot(W["long_video"], 7) == 4_294_983_680
+    assert tot(W["tf_dit"], 0) == 1_518_566_400
+    assert tot(W["long_tail"], 0) == tot(W["long_tail"], 3) == 304_747_728
+
+
+class _FakeTensor:
+    """Host-side stand-in with a data_ptr; the calls below fail validation
+    before any device access."""
+    def __init__(self, shape, dtype, ptr=0x1000, strides=None):
+        import torch
+        self.shape = shape
+        self.dtype = dtype
+        self._ptr = ptr
+        self._strides = strides or (shape[1] * shape[2], shape[2], 1)
+        self.torch = torch
+
+    def dim(self):
+        return 3
+
+    def stride(self, i):
+        return self._strides[i]
+
+    def data_ptr(self):
+        return self._ptr
+
+    def numel(self):
+        return 1 << 20
+
+    def element_size(self):
+        return 1
+
+
+def _fwd(q, k, v, out, step, mode=0, nseq=1, ws=None, cu=0x2000, lse=0x3000):
+    import context_attention_varlen_amd as m
+    ws = ws or _FakeTensor((1, 1, 1), None, ptr=0x4000)
+    return m._lib.cpattn_fwd_step(ctypes.byref(m._tensor(q)), ctypes.byref(m._tensor(k)),
+                                  ctypes.byref(m._tensor(v)), ctypes.c_void_p(cu), ctypes.c_void_p(cu), nseq,
+                                  mode, ctypes.byref(step), 0.0, ctypes.byref(m._tensor(out)),
+                                  ctypes.c_void_p(lse), ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+
+
+def test_fwd_step_rejects_bad_arguments():
+    import torch
+    bf = torch.bfloat16
+    q = _FakeTensor((64, 4, 128), bf)
+    kv = _FakeTensor((64, 2, 128), bf)
+    st = c.make_step(1, 0, 0)
+    assert _fwd(q, kv, kv, q, c.make_step(2, 2, 0)) == c.ERR_INVALID_ARG      # rank >= cp
+    assert _fwd(q, kv, kv, q, c.make_step(2, 0, 2)) == c.ERR_INVALID_ARG      # step >= cp
+    assert _fwd(q, _FakeTensor((64, 3, 128), bf), _FakeTensor((64, 3, 128), bf), q, st) == c.ERR_INVALID_ARG
+    assert _fwd(_FakeTensor((64, 4, 96), bf), kv, kv, q, st) == c.ERR_UNSUPPORTED  # head_dim
+    assert _fwd(q, _FakeTensor((64, 2, 128), torch.float32), kv, q, st) == c.ERR_INVALID_ARG  # mixed dtypes
+    assert _fwd(_FakeTensor((64, 4, 128), bf, ptr=0x1008), kv, kv, q, st) == c.ERR_INVALID_ARG  # misaligned
+    assert _fwd(q, kv, kv, q, st, cu=0) == c.ERR_INVALID_ARG                  # null cu_seqlens
+    assert _fwd(q, kv, kv, q, st, mode=2) == c.ERR_INVALID_ARG                # TF without B, N
+    assert _fwd(q, kv, kv, q, c.make_step(2, 0, 0, 8, 2), mode=2) == c.ERR_UNSUPPORTED  # TF with cp > 1
+    assert _fwd(q, kv, kv, q, st, mode=7) == c.ERR_INVALID_ARG                # unknown mask
+    small_ws = _FakeTensor((1, 1, 1), None, ptr=0x4000)
+    small_ws.numel = lambda: 16
+    assert _fwd(q, kv, kv, q, st, ws=small_ws) == c.ERR_WORKSPACE
+    overlap = _FakeTensor((64, 4, 128), bf, strides=(128, 64, 1))
+    assert _fwd(overlap, kv, kv, q, st) == c.ERR_INVALID_ARG                  # overlapping rows
+
+
+def test_workspace_size_monotone():
+    a = c.cpattn_workspace_size(1024, 1024, 4)
+    b = c.cpattn_workspace_size(32768, 32768, 4)
+    assert 0 < a < b and b % 256 == 0
