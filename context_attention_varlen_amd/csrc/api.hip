@@ -247,7 +247,7 @@ CPATTN_API cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_te
 
   const bool bf16 = q->dtype == CPATTN_BF16;
   const int d = q->head_dim;
-  const int tile_p = bf16 ? 128 : 64;
+  const int tile_p = fwd_tile_rows(bf16);
   const int64_t max_items = max_items_for(q->tokens, nseq, tile_p);
   const SchedArgs sa = sched_args(ws, L.total, cu_q, cu_k, nseq, q->tokens, k->tokens, step, step->rank,
                                   src_rank(step), true, mode, tile_p, 64, 1, max_items, L);
@@ -318,9 +318,60 @@ CPATTN_API cpattn_status cpattn_bwd_preprocess(const float* out, const cpattn_te
   return hip_status(launch_delta(a, (hipStream_t)stream));
 }
 
-CPATTN_API cpattn_status cpattn_bwd_step(const cpattn_tensor*, const cpattn_tensor*, const cpattn_tensor*,
-                                         const cpattn_tensor*, const float*, const float*, const int32_t*,
-                                         const int32_t*, int32_t, cpattn_mask_mode, const cpattn_step*, float,
-                                         float*, float*, float*, void*, size_t, void*) {
-  return CPATTN_ERR_UNSUPPORTED;
+CPATTN_API cpattn_status cpattn_bwd_step(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                         const cpattn_tensor* dout, const float* lse, const float* delta,
+                                         const int32_t* cu_q, const int32_t* cu_k, int32_t nseq,
+                                         cpattn_mask_mode mode, const cpattn_step* step, float scale, float* dq,
+                                         float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
+  cpattn_status st;
+  if ((st = check_tensor(q)) || (st = check_tensor(k)) || (st = check_tensor(v)) || (st = check_tensor(dout)))
+    return st;
+  if ((st = check_step(step, mode)) != CPATTN_OK) return st;
+  if (q->dtype != k->dtype || q->dtype != v->dtype || q->dtype != dout->dtype) return CPATTN_ERR_INVALID_ARG;
+  if (q->head_dim != k->head_dim || q->head_dim != v->head_dim || q->head_dim != dout->head_dim)
+    return CPATTN_ERR_INVALID_ARG;
+  if (k->heads != v->heads || q->heads != dout->heads || q->heads % k->heads) return CPATTN_ERR_INVALID_ARG;
+  if (q->tokens != dout->tokens || k->tokens != v->tokens) return CPATTN_ERR_INVALID_ARG;
+  if (!cu_q || !cu_k || nseq < 0) return CPATTN_ERR_INVALID_ARG;
+  if (q->tokens > 0 && (!lse || !delta || !dq || !aligned16(dq))) return CPATTN_ERR_INVALID_ARG;
+  if (k->tokens > 0 && (!dk || !dv || !aligned16(dk) || !aligned16(dv))) return CPATTN_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(q->tokens, k->tokens, nseq);
+  if (!ws || ws_bytes < L.total || !aligned16(ws)) return CPATTN_ERR_WORKSPACE;
+
+  const bool bf16 = q->dtype == CPATTN_BF16;
+  const int d = q->head_dim;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
+  const int grp = q->heads / k->heads;
+  hipStream_t s = (hipStream_t)stream;
+
+  BwdArgs a;
+  a.q = q->data; a.k = k->data; a.v = v->data; a.dout = dout->data;
+  a.q_st = q->stride_token; a.q_sh = q->stride_head;
+  a.k_st = k->stride_token; a.k_sh = k->stride_head;
+  a.v_st = v->stride_token; a.v_sh = v->stride_head;
+  a.do_st = dout->stride_token; a.do_sh = dout->stride_head;
+  a.lse = lse; a.delta = delta; a.tq = q->tokens;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.hq = q->heads; a.hkv = k->heads; a.grp = grp;
+  a.scale = sc; a.scale_log2 = sc * 1.4426950408889634f;
+  a.mask = (int)mode;
+
+  // dQ: query tiles against the step's keys
+  const int tq = bwd_dq_tile_rows(bf16);
+  const int64_t mq = max_items_for(q->tokens, nseq, tq);
+  SchedArgs sq = sched_args(ws, L.total, cu_q, cu_k, nseq, q->tokens, k->tokens, step, step->rank,
+                            src_rank(step), true, mode, tq, 64, 1, mq, L);
+  a.tf_b = sq.tf_b; a.tf_n = sq.tf_n;
+  a.hdr = sq.hdr; a.items = sq.items; a.order = sq.order;
+  if ((st = hip_status(launch_sched(sq, s))) != CPATTN_OK) return st;
+  if (nseq > 0 && q->tokens > 0 && (st = hip_status(launch_bwd_dq(a, bf16, d, mq, s))) != CPATTN_OK) return st;
+
+  // dK, dV: key tiles against the rank's queries (all q-heads of a group)
+  const int tk = bwd_dkv_tile_rows(bf16);
+  const int64_t mk = max_items_for(k->tokens, nseq, tk);
+  SchedArgs sk = sched_args(ws, L.total, cu_k, cu_q, nseq, k->tokens, q->tokens, step, src_rank(step),
+                            step->rank, false, mode, tk, 64, grp, mk, L);
+  if ((st = hip_status(launch_sched(sk, s))) != CPATTN_OK) return st;
+  if (nseq > 0 && k->tokens > 0) return hip_status(launch_bwd_dkv(a, bf16, d, mk, s));
+  return CPATTN_OK;
 }

@@ -1,0 +1,457 @@
+// Backward ring step, recomputing P from the final merged log-sum-exp.
+//
+// For the loss sum_i <dO_i, O_i>, with P_ij = exp(scale <q_i, k_j> - LSE_i)
+// and delta_i = <dO_i, O_i> (final O):
+//   dS_ij = P_ij (<dO_i, v_j> - delta_i)
+//   dQ_i += scale sum_j dS_ij k_j,  dK_j += scale sum_i dS_ij q_i,
+//   dV_j += sum_i P_ij dO_i
+// with j over the keys of the K/V share held at this ring step.  Training
+// through the ring ("Scaling Video Training with Parallelism", section 1:
+// splitting must not change the loss) needs exactly these per-step pieces;
+// the ring returns dK/dV of step s to their owner.
+//
+// Two kernels, no atomics, deterministic:
+//   dkv  one workgroup per (128-key tile, kv-head): 4 waves x 32 keys hold
+//        K and V as MFMA operands and dK^T, dV^T accumulators in registers,
+//        and sweep every q-head of the GQA group and every query tile that
+//        can see the keys (64 rows, Q/dO tiles in LDS, double-buffered):
+//          S = Q K^T, dP = dO V^T               (row reads of Q, dO)
+//          dV^T += dO^T P, dK^T += Q^T dS       (transposing reads of dO, Q)
+//   dq   one workgroup per (256-query tile, q-head): 4 waves x 64 queries
+//        hold Q, dO operands and dQ^T accumulators, sweeping key tiles:
+//          S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T
+// Each accumulator element is owned by one workgroup, so += is a plain
+// read-modify-write.  The fp32 path uses plain per-row kernels.
+#include "mfma.h"
+
+namespace cpattn {
+
+namespace {
+
+constexpr int kDqWaves = 4, kDqQB = 2;            // dq: 4 waves x 64 queries
+constexpr int kDkvWaves = 4;                       // dkv: 4 waves x 32 keys
+constexpr int kBwdBQ = 64;                         // query rows per LDS tile (dkv)
+constexpr int kBwdBK = 64;                         // key rows per LDS tile (dq)
+
+// ---------------------------------------------------------------------------
+// dq kernel (bf16)
+// ---------------------------------------------------------------------------
+template <int D, int NW, int QB>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
+  constexpr int BN = kBwdBK;
+  constexpr int QW = 32 * QB;
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][BN * D];
+
+  int item_rank, h, g;
+  map_block(blockIdx.x, a.grp, a.hkv, item_rank, h, g);
+  if (item_rank >= a.hdr->n_items) return;
+  const WorkItem it = a.items[a.order[item_rank]];
+  if (it.nseg == 0) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hh = lane >> 5;
+  const uint16_t* kbase = (const uint16_t*)a.k + (int64_t)g * a.k_sh;
+  const uint16_t* vbase = (const uint16_t*)a.v + (int64_t)g * a.v_sh;
+
+  const int nt0 = ceil_div(it.seg[0].n, BN);
+  const int nt1 = it.nseg > 1 ? ceil_div(it.seg[1].n, BN) : 0;
+  const int ntiles = nt0 + nt1;
+  auto issue = [&](int j) {
+    const int s = j < nt0 ? 0 : 1;
+    const int t0 = (j - (s ? nt0 : 0)) * BN;
+    const Segment& sg = it.seg[s];
+    load_tile<D, BN, NW>(s_k[j & 1], kbase, a.k_st, sg.row, t0, sg.n, wave, lane);
+    load_tile<D, BN, NW>(s_v[j & 1], vbase, a.v_st, sg.row, t0, sg.n, wave, lane);
+  };
+  issue(0);
+
+  bf16x8 qreg[QB][D / 16], doreg[QB][D / 16];
+  KeyRanges kr[QB];
+  bool row_ok[QB];
+  float lse2[QB], dlt[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r = wave * QW + qb * 32 + col;
+    row_ok[qb] = r < it.nrows;
+    kr[qb] = key_ranges(a.mask, it.pos0 + r, a.tf_b, a.tf_n);
+    const int64_t row = it.row0 + r;
+    const uint16_t* qs = (const uint16_t*)a.q + row * a.q_st + (int64_t)h * a.q_sh + 8 * hh;
+    const uint16_t* ds = (const uint16_t*)a.dout + row * a.do_st + (int64_t)h * a.do_sh + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 rq = {0u, 0u, 0u, 0u}, rd = {0u, 0u, 0u, 0u};
+      if (row_ok[qb]) {
+        rq = *(const u32x4*)(qs + 16 * ks);
+        rd = *(const u32x4*)(ds + 16 * ks);
+      }
+      qreg[qb][ks] = __builtin_bit_cast(bf16x8, rq);
+      doreg[qb][ks] = __builtin_bit_cast(bf16x8, rd);
+    }
+    float l = row_ok[qb] ? a.lse[(int64_t)h * a.tq + row] : -INFINITY;
+    lse2[qb] = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;   // P = 0 for rows with no key
+    dlt[qb] = row_ok[qb] ? a.delta[(int64_t)h * a.tq + row] : 0.f;
+  }
+
+  f32x16 acc[QB][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[qb][db][i] = 0.f;
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    wait_loads();
+    __syncthreads();
+    if (j + 1 < ntiles) issue(j + 1);
+    const int s = j < nt0 ? 0 : 1;
+    const int t0 = (j - (s ? nt0 : 0)) * BN;
+    const Segment sg = it.seg[s];
+    const uint16_t* tk = s_k[buf];
+    const uint16_t* tv = s_v[buf];
+    const bool full = t0 >= sg.full_lo && t0 + BN <= sg.full_hi;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      f32x16 st[QB], dpt[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { st[qb][i] = 0.f; dpt[qb][i] = 0.f; }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 ak = read_row8<D>(tk, kb * 32 + col, 2 * ks + hh);
+        const bf16x8 av = read_row8<D>(tv, kb * 32 + col, 2 * ks + hh);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          st[qb] = mfma32(ak, qreg[qb][ks], st[qb]);
+          dpt[qb] = mfma32(av, doreg[qb][ks], dpt[qb]);
+        }
+      }
+      if (!full) {
+        const int kb0 = t0 + kb * 32 + 4 * hh;
+        const int rem = sg.n - kb0;
+        const int pbase = sg.pos + kb0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int off = 8 * (i >> 2) + (i & 3);
+          const bool in = off < rem;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            if (!(in && in_ranges(kr[qb], pbase + off))) st[qb][i] = -INFINITY;
+        }
+      }
+      bf16x8 dsb[QB][2];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(st[qb][i] * a.scale_log2 - lse2[qb]);
+          st[qb][i] = p * (dpt[qb][i] - dlt[qb]);
+        }
+        dsb[qb][0] = pack_b(st[qb], 0);
+        dsb[qb][1] = pack_b(st[qb], 1);
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const bf16x8 akt = read_tr<D>(tk, 32 * kb + 16 * hs, 32 * db, lane);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(akt, dsb[qb][hs], acc[qb][db]);
+        }
+    }
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (!row_ok[qb]) continue;
+    const int r = wave * QW + qb * 32 + col;
+    float* dst = a.dq + ((int64_t)(it.row0 + r) * a.hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4* p = (f32x4*)(dst + db * 32 + 8 * i4 + 4 * hh);
+        f32x4 v = *p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += a.scale * acc[qb][db][4 * i4 + e];
+        *p = v;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dkv kernel (bf16)
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dkv_bf16_kernel(BwdArgs a) {
+  constexpr int BQ = kBwdBQ;
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_do[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];
+  __shared__ __attribute__((aligned(16))) float s_dl[2][BQ];
+
+  int item_rank, hdummy, g;
+  map_block(blockIdx.x, 1, a.hkv, item_rank, hdummy, g);
+  if (item_rank >= a.hdr->n_items) return;
+  const WorkItem it = a.items[a.order[item_rank]];
+  if (it.nseg == 0) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, hh = lane >> 5;
+  const int kr_ = wave * 32 + col;                  // key row in the tile
+  const bool key_ok = kr_ < it.nrows;
+  const KeyRanges qrng = query_ranges(a.mask, it.pos0 + kr_, a.tf_b, a.tf_n);
+
+  // K, V as B operands (B[k = d][n = key]): lane holds X[key][16*ks + 8*hh + 0..7]
+  bf16x8 kreg[D / 16], vreg[D / 16];
+  {
+    const int64_t row = it.row0 + kr_;
+    const uint16_t* ks_ = (const uint16_t*)a.k + row * a.k_st + (int64_t)g * a.k_sh + 8 * hh;
+    const uint16_t* vs_ = (const uint16_t*)a.v + row * a.v_st + (int64_t)g * a.v_sh + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
+      if (key_ok) {
+        rk = *(const u32x4*)(ks_ + 16 * ks);
+        rv = *(const u32x4*)(vs_ + 16 * ks);
+      }
+      kreg[ks] = __builtin_bit_cast(bf16x8, rk);
+      vreg[ks] = __builtin_bit_cast(bf16x8, rv);
+    }
+  }
+
+  const int nt0 = ceil_div(it.seg[0].n, BQ);
+  const int nt1 = it.nseg > 1 ? ceil_div(it.seg[1].n, BQ) : 0;
+  const int per_head = nt0 + nt1;
+  const int ntiles = per_head * a.grp;
+  auto tile_of = [&](int j, int& h, int& s, int& t0) {
+    const int jh = j / per_head, jt = j - jh * per_head;
+    h = g * a.grp + jh;
+    s = jt < nt0 ? 0 : 1;
+    t0 = (jt - (s ? nt0 : 0)) * BQ;
+  };
+  auto issue = [&](int j) {
+    int h, s, t0;
+    tile_of(j, h, s, t0);
+    const Segment& sg = it.seg[s];
+    const uint16_t* qb = (const uint16_t*)a.q + (int64_t)h * a.q_sh;
+    const uint16_t* db = (const uint16_t*)a.dout + (int64_t)h * a.do_sh;
+    load_tile<D, BQ, NW>(s_q[j & 1], qb, a.q_st, sg.row, t0, sg.n, wave, lane);
+    load_tile<D, BQ, NW>(s_do[j & 1], db, a.do_st, sg.row, t0, sg.n, wave, lane);
+    if (wave < 2) {
+      const int r = min(t0 + lane, sg.n - 1);
+      const float* src = (wave == 0 ? a.lse : a.delta) + (int64_t)h * a.tq + sg.row + r;
+      float* dst = wave == 0 ? s_lse[j & 1] : s_dl[j & 1];
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+    }
+  };
+  issue(0);
+
+  f32x16 acc_k[D / 32], acc_v[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { acc_k[db][i] = 0.f; acc_v[db][i] = 0.f; }
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    wait_loads();
+    __syncthreads();
+    if (j + 1 < ntiles) issue(j + 1);
+    int h, s, t0;
+    tile_of(j, h, s, t0);
+    const Segment sg = it.seg[s];
+    const uint16_t* tq = s_q[buf];
+    const uint16_t* tdo = s_do[buf];
+    const bool full = t0 >= sg.full_lo && t0 + BQ <= sg.full_hi;
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      // S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys
+      f32x16 st, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { st[i] = 0.f; dp[i] = 0.f; }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 aq = read_row8<D>(tq, qb * 32 + col, 2 * ks + hh);
+        const bf16x8 ad = read_row8<D>(tdo, qb * 32 + col, 2 * ks + hh);
+        st = mfma32(aq, kreg[ks], st);
+        dp = mfma32(ad, vreg[ks], dp);
+      }
+      // rows of this lane: q = qb*32 + 8*(i/4) + 4*hh + i%4
+      const int qb0 = qb * 32 + 4 * hh;
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        l4[i4] = *(const f32x4*)(&s_lse[buf][qb0 + 8 * i4]);
+        d4[i4] = *(const f32x4*)(&s_dl[buf][qb0 + 8 * i4]);
+      }
+      const int qofs0 = t0 + qb0;
+      const int rem = sg.n - qofs0;
+      const int pbase = sg.pos + qofs0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int off = 8 * (i >> 2) + (i & 3);
+        const float l = l4[i >> 2][i & 3];
+        const float lse2 = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
+        float p = __builtin_amdgcn_exp2f(st[i] * a.scale_log2 - lse2);
+        if (!full && !(off < rem && in_ranges(qrng, pbase + off))) p = 0.f;
+        st[i] = p;
+        dp[i] = p * (dp[i] - d4[i >> 2][i & 3]);
+      }
+      bf16x8 pb[2], dsb[2];
+      pb[0] = pack_b(st, 0);
+      pb[1] = pack_b(st, 1);
+      dsb[0] = pack_b(dp, 0);
+      dsb[1] = pack_b(dp, 1);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const bf16x8 adt = read_tr<D>(tdo, 32 * qb + 16 * hs, 32 * db, lane);
+          const bf16x8 aqt = read_tr<D>(tq, 32 * qb + 16 * hs, 32 * db, lane);
+          acc_v[db] = mfma32(adt, pb[hs], acc_v[db]);
+          acc_k[db] = mfma32(aqt, dsb[hs], acc_k[db]);
+        }
+    }
+    (void)h;
+  }
+
+  if (!key_ok) return;
+  const int64_t row = it.row0 + kr_;
+  float* dkp = a.dk + (row * a.hkv + g) * D;
+  float* dvp = a.dv + (row * a.hkv + g) * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int off = db * 32 + 8 * i4 + 4 * hh;
+      f32x4 vk = *(f32x4*)(dkp + off), vv = *(f32x4*)(dvp + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vk[e] += a.scale * acc_k[db][4 * i4 + e];
+        vv[e] += acc_v[db][4 * i4 + e];
+      }
+      *(f32x4*)(dkp + off) = vk;
+      *(f32x4*)(dvp + off) = vv;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: one row per thread.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdArgs a) {
+  int item_rank, h, g;
+  map_block(blockIdx.x, a.grp, a.hkv, item_rank, h, g);
+  if (item_rank >= a.hdr->n_items) return;
+  const WorkItem it = a.items[a.order[item_rank]];
+  const int r = threadIdx.x;
+  if (r >= it.nrows) return;
+  const int64_t row = it.row0 + r;
+  const int pq = it.pos0 + r;
+  const float* qp = (const float*)a.q + row * a.q_st + (int64_t)h * a.q_sh;
+  const float* dop = (const float*)a.dout + row * a.do_st + (int64_t)h * a.do_sh;
+  const float l = a.lse[(int64_t)h * a.tq + row];
+  if (l == -INFINITY) return;
+  const float dl = a.delta[(int64_t)h * a.tq + row];
+  float qv[D], dov[D], acc[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) { qv[c] = qp[c]; dov[c] = dop[c]; acc[c] = 0.f; }
+  for (int s = 0; s < it.nseg; ++s) {
+    const Segment sg = it.seg[s];
+    for (int kk = 0; kk < sg.n; ++kk) {
+      if (!mask_allowed(a.mask, pq, sg.pos + kk, a.tf_b, a.tf_n)) continue;
+      const float* kr = (const float*)a.k + (int64_t)(sg.row + kk) * a.k_st + (int64_t)g * a.k_sh;
+      const float* vr = (const float*)a.v + (int64_t)(sg.row + kk) * a.v_st + (int64_t)g * a.v_sh;
+      float sdot = 0.f, pdot = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) { sdot = fmaf(qv[c], kr[c], sdot); pdot = fmaf(dov[c], vr[c], pdot); }
+      const float p = expf(sdot * a.scale - l);
+      const float ds = p * (pdot - dl);
+#pragma unroll
+      for (int c = 0; c < D; ++c) acc[c] = fmaf(ds, kr[c], acc[c]);
+    }
+  }
+  float* dst = a.dq + (row * a.hq + h) * D;
+#pragma unroll
+  for (int c = 0; c < D; ++c) dst[c] += a.scale * acc[c];
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void bwd_dkv_f32_kernel(BwdArgs a) {
+  int item_rank, hdummy, g;
+  map_block(blockIdx.x, 1, a.hkv, item_rank, hdummy, g);
+  if (item_rank >= a.hdr->n_items) return;
+  const WorkItem it = a.items[a.order[item_rank]];
+  const int r = threadIdx.x;
+  if (r >= it.nrows) return;
+  const int64_t row = it.row0 + r;
+  const int pk = it.pos0 + r;
+  const float* kp = (const float*)a.k + row * a.k_st + (int64_t)g * a.k_sh;
+  const float* vp = (const float*)a.v + row * a.v_st + (int64_t)g * a.v_sh;
+  float kv[D], vv[D], ak[D], av[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) { kv[c] = kp[c]; vv[c] = vp[c]; ak[c] = 0.f; av[c] = 0.f; }
+  for (int jh = 0; jh < a.grp; ++jh) {
+    const int h = g * a.grp + jh;
+    for (int s = 0; s < it.nseg; ++s) {
+      const Segment sg = it.seg[s];
+      for (int qq = 0; qq < sg.n; ++qq) {
+        if (!mask_allowed(a.mask, sg.pos + qq, pk, a.tf_b, a.tf_n)) continue;
+        const int64_t qrow = sg.row + qq;
+        const float l = a.lse[(int64_t)h * a.tq + qrow];
+        if (l == -INFINITY) continue;
+        const float* qr = (const float*)a.q + qrow * a.q_st + (int64_t)h * a.q_sh;
+        const float* dr = (const float*)a.dout + qrow * a.do_st + (int64_t)h * a.do_sh;
+        float sdot = 0.f, pdot = 0.f;
+#pragma unroll
+        for (int c = 0; c < D; ++c) { sdot = fmaf(qr[c], kv[c], sdot); pdot = fmaf(dr[c], vv[c], pdot); }
+        const float p = expf(sdot * a.scale - l);
+        const float ds = p * (pdot - a.delta[(int64_t)h * a.tq + qrow]);
+#pragma unroll
+        for (int c = 0; c < D; ++c) { ak[c] = fmaf(ds, qr[c], ak[c]); av[c] = fmaf(p, dr[c], av[c]); }
+      }
+    }
+  }
+  float* dkp = a.dk + (row * a.hkv + g) * D;
+  float* dvp = a.dv + (row * a.hkv + g) * D;
+#pragma unroll
+  for (int c = 0; c < D; ++c) { dkp[c] += a.scale * ak[c]; dvp[c] += av[c]; }
+}
+
+}  // namespace
+
+int bwd_dq_tile_rows(bool bf16) { return bf16 ? 32 * kDqQB * kDqWaves : 64; }
+int bwd_dkv_tile_rows(bool bf16) { return bf16 ? 32 * kDkvWaves : 64; }
+
+hipError_t launch_bwd_dq(const BwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream) {
+  const dim3 grid(unit_grid(max_items, a.hkv, a.grp));
+  if (bf16) {
+    if (d == 128) hipLaunchKernelGGL((bwd_dq_bf16_kernel<128, kDqWaves, kDqQB>), grid, dim3(64 * kDqWaves), 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dq_bf16_kernel<64, kDqWaves, kDqQB>), grid, dim3(64 * kDqWaves), 0, stream, a);
+  } else {
+    if (d == 128) hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, grid, dim3(64), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkv(const BwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream) {
+  const dim3 grid(unit_grid(max_items, a.hkv, 1));
+  if (bf16) {
+    if (d == 128) hipLaunchKernelGGL((bwd_dkv_bf16_kernel<128, kDkvWaves>), grid, dim3(64 * kDkvWaves), 0, stream, a);
+    else hipLaunchKernelGGL((bwd_dkv_bf16_kernel<64, kDkvWaves>), grid, dim3(64 * kDkvWaves), 0, stream, a);
+  } else {
+    if (d == 128) hipLaunchKernelGGL(bwd_dkv_f32_kernel<128>, grid, dim3(64), 0, stream, a);
+    else hipLaunchKernelGGL(bwd_dkv_f32_kernel<64>, grid, dim3(64), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

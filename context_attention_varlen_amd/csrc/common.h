@@ -111,6 +111,26 @@ struct FwdArgs {
   const int32_t* order;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, do_st, do_sh;
+  const float* lse;     // [Hq][Tq]
+  const float* delta;   // [Hq][Tq]
+  int64_t tq;
+  float* dq;            // [Tq][Hq][D] +=
+  float* dk;            // [Tk][Hkv][D] +=
+  float* dv;
+  int hq, hkv, grp;
+  float scale, scale_log2;
+  int mask, tf_b, tf_n;
+  const WsHeader* hdr;
+  const WorkItem* items;
+  const int32_t* order;
+};
+
 struct MergeArgs {
   float* out;
   float* lse;
@@ -150,6 +170,11 @@ struct PartArgs {
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream);
+int fwd_tile_rows(bool bf16);
+int bwd_dq_tile_rows(bool bf16);
+int bwd_dkv_tile_rows(bool bf16);
+hipError_t launch_bwd_dq(const BwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream);
+hipError_t launch_bwd_dkv(const BwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_delta(const DeltaArgs& a, hipStream_t stream);
 hipError_t launch_partition(const PartArgs& a, hipStream_t stream);
@@ -177,6 +202,72 @@ __device__ __forceinline__ bool mask_allowed(int mode, int32_t pq, int32_t pk, i
   const int32_t ck = (kn ? pk - span : pk) / tf_b;
   if (!qn) return !kn && ck <= cq;
   return kn ? ck == cq : ck < cq;
+}
+
+// The keys a query at position pq may attend, as at most two position
+// intervals: p is allowed iff (unsigned)(p - lo1) < len1 or
+// (unsigned)(p - lo2) < len2.  Same predicate as mask_allowed.
+struct KeyRanges {
+  unsigned lo1, len1, lo2, len2;
+};
+
+__device__ __forceinline__ KeyRanges key_ranges(int mode, int32_t pq, int32_t tf_b, int32_t tf_n) {
+  KeyRanges r;
+  r.lo2 = 0u;
+  r.len2 = 0u;
+  if (mode == CPATTN_MASK_CAUSAL) {
+    r.lo1 = 0u;
+    r.len1 = (unsigned)(pq + 1);
+  } else if (mode == CPATTN_MASK_BIDIR) {
+    r.lo1 = 0u;
+    r.len1 = 0xffffffffu;
+  } else {
+    const int32_t span = tf_b * tf_n;
+    if (pq < span) {                      // clean chunk c: clean chunks <= c
+      r.lo1 = 0u;
+      r.len1 = (unsigned)((pq / tf_b + 1) * tf_b);
+    } else {                              // noisy chunk c: clean < c, noisy == c
+      const int32_t c = (pq - span) / tf_b;
+      r.lo1 = 0u;
+      r.len1 = (unsigned)(c * tf_b);
+      r.lo2 = (unsigned)(span + c * tf_b);
+      r.len2 = (unsigned)tf_b;
+    }
+  }
+  return r;
+}
+
+// The queries that may attend a key at position pk (the transpose of
+// key_ranges), as at most two position intervals.
+__device__ __forceinline__ KeyRanges query_ranges(int mode, int32_t pk, int32_t tf_b, int32_t tf_n) {
+  KeyRanges r;
+  r.lo2 = 0u;
+  r.len2 = 0u;
+  if (mode == CPATTN_MASK_CAUSAL) {
+    r.lo1 = (unsigned)pk;
+    r.len1 = 0x7fffffffu;
+  } else if (mode == CPATTN_MASK_BIDIR) {
+    r.lo1 = 0u;
+    r.len1 = 0xffffffffu;
+  } else {
+    const int32_t span = tf_b * tf_n;
+    if (pk < span) {                      // clean chunk c: clean >= c, noisy > c
+      const int32_t c = pk / tf_b;
+      r.lo1 = (unsigned)(c * tf_b);
+      r.len1 = (unsigned)(span - c * tf_b);
+      r.lo2 = (unsigned)(span + (c + 1) * tf_b);
+      r.len2 = (unsigned)(span - (c + 1) * tf_b);
+    } else {                              // noisy chunk c: noisy == c
+      const int32_t c = (pk - span) / tf_b;
+      r.lo1 = (unsigned)(span + c * tf_b);
+      r.len1 = (unsigned)tf_b;
+    }
+  }
+  return r;
+}
+
+__device__ __forceinline__ bool in_ranges(const KeyRanges& r, int32_t pk) {
+  return ((unsigned)pk - r.lo1 < r.len1) | ((unsigned)pk - r.lo2 < r.len2);
 }
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
