@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of one context-parallel rank's blockwise (zigzag ring) attention
+hot path on one MI355X.
+
+A step is one pass of the whole path over one synthetic packed batch that is
+already resident in HBM:
+    zigzag partition of Q, dO (this rank) and K, V (every source rank)
+    for each ring step: tile scheduler + forward step, then LSE merge
+    backward preprocess (delta), then for each ring step: backward step
+Workload (default): the long-tail packed microbatch -- 65536 tokens, one
+49152-token sequence plus 15 short ones, causal, zigzag cp=4, rank 0,
+Hq=32 / Hkv=8, d=128, bf16.
+
+FLOPs are causal-adjusted: counted from the exact number of allowed
+(query, key) pairs (cpattn_count_pairs), forward 4*d*Hq per pair and
+backward 10*d*Hq per pair, never from max_seqlen.
+
+Prints one JSON line.  Only N=1 is measured: this build targets one GPU.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="long_tail")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true")
+    return p.parse_args()
+
+
+class Timer:
+    """Per-call durations with events on the launch stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.events = {}
+
+    def __call__(self, name, fn):
+        t = self.torch
+        a = t.cuda.Event(enable_timing=True)
+        b = t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.events.setdefault(name, []).append((a, b))
+
+    def stats(self):
+        out = {}
+        for k, evs in self.events.items():
+            ms = [a.elapsed_time(b) for a, b in evs]
+            out[k] = {"calls": len(ms), "total_ms": sum(ms), "avg_ms": sum(ms) / len(ms)}
+        return out
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "context_attention_varlen_amd", "csrc"))):
+        h.update(open(os.path.join(ROOT, "context_attention_varlen_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed counter summary, only if it was
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    ent = rec.get(kernel)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def run_hot_path(c, torch, w, steps, warmup):
+    import numpy as np
+
+    import workloads
+    from context_attention_varlen_amd.ring import ForwardBuffers, RankPlan
+
+    x = workloads.draw(w)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = {k: torch.from_numpy(v).to(td).cuda() for k, v in x.items()}
+    plan = RankPlan.make(w.cu_seqlens, w.cp, w.rank)
+    tl = plan.tokens_local
+    q = torch.empty((tl, w.heads_q, w.head_dim), dtype=td, device="cuda")
+    do = torch.empty_like(q) if w.backward else None
+    ks = [torch.empty((tl, w.heads_kv, w.head_dim), dtype=td, device="cuda") for _ in range(w.cp)]
+    vs = [torch.empty_like(ks[0]) for _ in range(w.cp)]
+    bufs = ForwardBuffers.make(q, tl, plan.num_seqs)
+    if w.backward:
+        dq = torch.zeros((tl, w.heads_q, w.head_dim), dtype=torch.float32, device="cuda")
+        dk = [torch.zeros(ks[0].shape, dtype=torch.float32, device="cuda") for _ in range(w.cp)]
+        dv = [torch.zeros(ks[0].shape, dtype=torch.float32, device="cuda") for _ in range(w.cp)]
+        delta = torch.empty((w.heads_q, tl), dtype=torch.float32, device="cuda")
+    tf = (w.tf_chunk, w.tf_num)
+    steps_ = [c.make_step(w.cp, w.rank, s, *tf) for s in range(w.cp)]
+    r = w.rank
+    cu_g, nseq = plan.cu_global_dev, plan.num_seqs
+
+    def step(tm):
+        tm("partition", lambda: c.cpattn_partition(g["q"], q, cu_g, nseq, w.cp, r))
+        if w.backward:
+            tm("partition", lambda: c.cpattn_partition(g["dout"], do, cu_g, nseq, w.cp, r))
+        for j in range(w.cp):
+            tm("partition", lambda j=j: c.cpattn_partition(g["k"], ks[j], cu_g, nseq, w.cp, j))
+            tm("partition", lambda j=j: c.cpattn_partition(g["v"], vs[j], cu_g, nseq, w.cp, j))
+        bufs.reset()
+        for s in range(w.cp):
+            j = (r - s) % w.cp
+            tm("fwd_step", lambda s=s, j=j: c.cpattn_fwd_step(
+                q, ks[j], vs[j], plan.cu_local_dev, plan.cu_local_dev, nseq, w.mask, steps_[s], 0.0,
+                bufs.out_partial, bufs.lse_partial, bufs.workspace))
+            tm("merge", lambda: c.cpattn_merge(bufs.out, bufs.lse, bufs.out_partial, bufs.lse_partial))
+        if w.backward:
+            dq.zero_()
+            for t_ in dk + dv:
+                t_.zero_()
+            tm("bwd_preprocess", lambda: c.cpattn_bwd_preprocess(bufs.out, do, delta))
+            for s in range(w.cp):
+                j = (r - s) % w.cp
+                tm("bwd_step", lambda s=s, j=j: c.cpattn_bwd_step(
+                    q, ks[j], vs[j], do, bufs.lse, delta, plan.cu_local_dev, plan.cu_local_dev, nseq, w.mask,
+                    steps_[s], 0.0, dq, dk[j], dv[j], bufs.workspace))
+
+    null = lambda name, fn: fn()  # noqa: E731
+    for _ in range(warmup):
+        step(null)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(tm)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ok = bool(torch.isfinite(bufs.out).all().item()) and (not w.backward or bool(torch.isfinite(dq).all().item()))
+    pairs = [c.cpattn_count_pairs(w.cu_seqlens, w.mask, st) for st in steps_]
+    # live partial rows per step (rows with at least one key), for merge bytes
+    return wall_ms, tm.stats(), pairs, ok, x
+
+
+def cpu_baseline(w, x, rows=256):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    `rows` seeded query rows of the rank (all q-heads), forward and backward
+    against every key they may attend."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                   default=1)
+    except Exception:  # pragma: no cover
+        blas = 1
+    cu = w.cu_seqlens
+    _, l2g, qpos, qseq = oracle.local_rows(cu, w.cp, w.rank)
+    rng = np.random.default_rng(1005)
+    sel = np.sort(rng.choice(len(l2g), size=min(rows, len(l2g)), replace=False))
+    T = int(cu[-1])
+    seq = np.repeat(np.arange(len(cu) - 1), np.diff(cu))
+    pos = np.arange(T) - cu[seq]
+    keep = np.isin(seq, np.unique(qseq[sel]))
+    t0 = time.perf_counter()
+    o, lse = oracle.attention(x["q"][l2g[sel]], x["k"][keep], x["v"][keep], qseq[sel], qpos[sel], seq[keep],
+                              pos[keep], w.mask, tf_chunk=w.tf_chunk, tf_num=w.tf_num)
+    if w.backward:
+        delta = oracle.bwd_delta(o, x["dout"][l2g[sel]])
+        oracle.attention_backward(x["q"][l2g[sel]], x["k"][keep], x["v"][keep], x["dout"][l2g[sel]], lse, delta,
+                                  qseq[sel], qpos[sel], seq[keep], pos[keep], w.mask,
+                                  tf_chunk=w.tf_chunk, tf_num=w.tf_num)
+    dt = time.perf_counter() - t0
+    pairs = int(sum(oracle.allowed(w.mask, qpos[i], pos[(seq == qseq[i])], w.tf_chunk, w.tf_num).sum()
+                    for i in sel))
+    per_pair = (4 + (10 if w.backward else 0)) * w.head_dim * w.heads_q
+    return {"value": round(pairs * per_pair / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{len(sel)} seeded query rows of rank {w.rank} ({w.heads_q} q-heads), "
+                      f"{'forward+backward' if w.backward else 'forward'} against all {pairs} allowed "
+                      f"(query, key) pairs per head, fp64 NumPy"}
+
+
+def extras(c, torch):
+    """Forward and merge figures of the other workloads (not part of `value`)."""
+    import workloads
+    from context_attention_varlen_amd.ring import ForwardBuffers, RankPlan, partition
+    out = {}
+    gen = torch.Generator(device="cuda")
+    for name in ("packed_varlen", "long_video", "tf_dit"):
+        w = workloads.WORKLOADS[name]
+        gen.manual_seed(0)
+        plan = RankPlan.make(w.cu_seqlens, w.cp, w.rank)
+        mk = lambda h: (torch.randn((w.tokens, h, w.head_dim), device="cuda", generator=gen)  # noqa: E731
+                        * w.value_scale).bfloat16()
+        qg, kg, vg = mk(w.heads_q), mk(w.heads_kv), mk(w.heads_kv)
+        q = partition(qg, plan)
+        ks = [partition(kg, plan, j) for j in range(w.cp)]
+        vs = [partition(vg, plan, j) for j in range(w.cp)]
+        del qg, kg, vg
+        bufs = ForwardBuffers.make(q, ks[0].shape[0], plan.num_seqs)
+        tf = (w.tf_chunk, w.tf_num)
+        sts = [c.make_step(w.cp, w.rank, s, *tf) for s in range(w.cp)]
+        pairs = sum(c.cpattn_count_pairs(w.cu_seqlens, w.mask, st) for st in sts)
+        tm = Timer(torch)
+        for it in range(4):
+            bufs.reset()
+            for s in range(w.cp):
+                j = (w.rank - s) % w.cp
+                f = lambda s=s, j=j: c.cpattn_fwd_step(q, ks[j], vs[j], plan.cu_local_dev, plan.cu_local_dev,  # noqa
+                                                       plan.num_seqs, w.mask, sts[s], 0.0, bufs.out_partial,
+                                                       bufs.lse_partial, bufs.workspace)
+                (tm if it else (lambda n, fn: fn()))("fwd", f)
+                c.cpattn_merge(bufs.out, bufs.lse, bufs.out_partial, bufs.lse_partial)
+        torch.cuda.synchronize()
+        st = tm.stats()["fwd"]
+        ms = st["total_ms"] / 3
+        tfl = 4 * w.head_dim * w.heads_q * pairs / (ms * 1e-3) / 1e12
+        out[name] = {"fwd_ms": round(ms, 3), "fwd_tflops": round(tfl, 1),
+                     "pct_peak": round(100 * tfl / PEAK_BF16_TFLOPS, 1), "pairs_per_head": pairs}
+        if name == "long_video":
+            # merge with every partial row live (finite lse_partial)
+            bufs.lse_partial.normal_()
+            tm2 = Timer(torch)
+            for it in range(6):
+                (tm2 if it else (lambda n, fn: fn()))("merge", lambda: c.cpattn_merge(
+                    bufs.out, bufs.lse, bufs.out_partial, bufs.lse_partial))
+            torch.cuda.synchronize()
+            mst = tm2.stats()["merge"]
+            rows = q.shape[0] * w.heads_q
+            nbytes = rows * (8 * w.head_dim + 2 * w.head_dim + 12)
+            out["merge_long_video_all_live"] = {
+                "avg_ms": round(mst["avg_ms"], 4), "bytes": nbytes,
+                "gbps": round(nbytes / (mst["avg_ms"] * 1e-3) / 1e9, 1),
+                "pct_peak_hbm": round(100 * nbytes / (mst["avg_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 1)}
+        del q, ks, vs, bufs
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs one rank's share "
+              "on one MI355X and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import context_attention_varlen_amd as c
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    wall_ms, st, pairs, finite, x = run_hot_path(c, torch, w, args.steps, args.warmup)
+    P = sum(pairs)
+    fwd_flops = 4 * w.head_dim * w.heads_q * P
+    bwd_flops = 10 * w.head_dim * w.heads_q * P if w.backward else 0
+    tflops = (fwd_flops + bwd_flops) / (wall_ms * 1e-3) / 1e12
+
+    # dominant kernel and its roofline
+    kern = {"fwd_step": ("cpattn::fwd_bf16_kernel<128, 4, 2>", fwd_flops / w.cp),
+            "bwd_step": ("cpattn::(anonymous namespace)::bwd_bf16_kernel<128>", bwd_flops / w.cp)}
+    dom = max((k for k in kern if k in st), key=lambda k: st[k]["total_ms"])
+    kname, flops_per_launch = kern[dom]
+    avg_ms = st[dom]["avg_ms"]
+    achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(kname), "avg_launch_ms": round(avg_ms, 4),
+                "algorithmic_flops_per_launch": int(flops_per_launch)}
+
+    per_call = {k: {"calls_per_step": v["calls"] // args.steps, "avg_ms": round(v["avg_ms"], 4),
+                    "ms_per_step": round(v["total_ms"] / args.steps, 4)} for k, v in st.items()}
+    fwd_ms = st["fwd_step"]["total_ms"] / args.steps
+    per_call["fwd_step"]["tflops"] = round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 1)
+    if "bwd_step" in st:
+        bwd_ms = st["bwd_step"]["total_ms"] / args.steps
+        per_call["bwd_step"]["tflops"] = round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1)
+
+    rec = {
+        "metric": "blockwise attn TFLOP/s (causal-adjusted) + % of bf16 MFMA peak, 1 MI355X",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16; long-tail lengths drawn as in workloads/)",
+        "config": {"workload": f"{w.name}: {w.tokens} tokens ({len(w.seqlens)} sequences, longest "
+                               f"{max(w.seqlens)}), causal zigzag cp={w.cp} rank {w.rank}, "
+                               f"Hq={w.heads_q}/Hkv={w.heads_kv}, d={w.head_dim}, "
+                               f"{'forward+backward' if w.backward else 'forward'}",
+                   "global_batch": 1, "seq_len": w.tokens, "tokens_local": w.tokens // w.cp,
+                   "parallelism": f"cp{w.cp} (one rank's share on one GPU)"},
+        "pairs_per_head": P, "flops_per_step": fwd_flops + bwd_flops, "outputs_finite": finite,
+        "per_call": per_call, "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, x)
+    if not args.no_extras:
+        rec["extras"] = extras(c, torch)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

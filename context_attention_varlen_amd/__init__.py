@@ -25,7 +25,7 @@ F32, BF16 = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTS = (
-    "cpattn_version", "cpattn_status_string", "cpattn_partition_index", "cpattn_partition",
+    "cpattn_version", "cpattn_status_string", "cpattn_last_hip_error", "cpattn_partition_index", "cpattn_partition",
     "cpattn_unpartition", "cpattn_count_pairs", "cpattn_workspace_size", "cpattn_workspace_status",
     "cpattn_fwd_step", "cpattn_merge", "cpattn_bwd_preprocess", "cpattn_bwd_step",
 )
@@ -34,7 +34,10 @@ EXPORTS = (
 class CpattnError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
-        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        msg = f"{where}: {status_string(status)} (status {status})"
+        if status == ERR_HIP:
+            msg += f": {_lib.cpattn_last_hip_error().decode()}"
+        super().__init__(msg)
 
 
 class Tensor(ctypes.Structure):
@@ -49,6 +52,11 @@ class Step(ctypes.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime (libamdhip64).  Load it first so that
+    # libcpattn binds to the same runtime instance: the stream handles and
+    # device pointers torch hands over are only meaningful there, and two
+    # runtimes in one process do not share the device.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libcpattn.so not built at {LIB_PATH}; run python -m context_attention_varlen_amd.build")
     lib = ctypes.CDLL(LIB_PATH)
@@ -58,6 +66,7 @@ def _load():
     sig = {
         "cpattn_version": (ctypes.c_char_p, []),
         "cpattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "cpattn_last_hip_error": (ctypes.c_char_p, []),
         "cpattn_partition_index": (ctypes.c_int, [P, I32, I32, I32, P, P]),
         "cpattn_partition": (ctypes.c_int, [TP, TP, P, I32, I32, I32, P]),
         "cpattn_unpartition": (ctypes.c_int, [TP, TP, P, I32, I32, I32, P]),

@@ -1,6 +1,8 @@
 """Build libcpattn.so (hand-written HIP for gfx950) in-tree with hipcc.
 
-    python -m context_attention_varlen_amd.build
+    python context_attention_varlen_amd/build.py
+
+(run as a script, not with -m: importing the package loads the library.)
 """
 import os
 import subprocess

@@ -2,6 +2,7 @@
 // checks its arguments before anything is enqueued; no C++ exception leaves
 // this file.
 #include <cmath>
+#include <cstdio>
 #include <cstring>
 #include <new>
 
@@ -51,7 +52,17 @@ cpattn_status check_step(const cpattn_step* s, cpattn_mask_mode mode) {
 
 int src_rank(const cpattn_step* s) { return ((s->rank - s->step) % s->cp + s->cp) % s->cp; }
 
-cpattn_status hip_status(hipError_t e) { return e == hipSuccess ? CPATTN_OK : CPATTN_ERR_HIP; }
+thread_local char g_last_hip_error[256] = "";
+
+cpattn_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return CPATTN_OK;
+  snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s (%d)", hipGetErrorString(e), (int)e);
+  return CPATTN_ERR_HIP;
+}
+
+// A runtime error left by an unrelated earlier call on this thread must not
+// be reported as the failure of our launch: clear it before enqueueing.
+void clear_stale_error() { (void)hipGetLastError(); }
 
 // Host closed form: pairs (p, k), p in [a, a+C), k in [b, b+Cb), k <= p.
 int64_t causal_block_pairs(int64_t a, int64_t C, int64_t b, int64_t Cb) {
@@ -66,11 +77,10 @@ int64_t causal_block_pairs(int64_t a, int64_t C, int64_t b, int64_t Cb) {
 }
 
 // Shared set-up of the scheduler arguments.
-SchedArgs sched_args(void* ws, int64_t ws_bytes_needed, const int32_t* cu_p, const int32_t* cu_s, int nseq,
-                     int64_t tok_p, int64_t tok_s, const cpattn_step* st, int rank_p, int rank_s,
-                     bool primary_is_q, cpattn_mask_mode mode, int tile_p, int tile_s, int cost_mult,
-                     int64_t max_items, const WsLayout& L) {
-  (void)ws_bytes_needed;
+SchedArgs sched_args(void* ws, const int32_t* cu_p, const int32_t* cu_s, int nseq, int64_t tok_p,
+                     int64_t tok_s, const cpattn_step* st, int rank_p, int rank_s, bool primary_is_q,
+                     cpattn_mask_mode mode, int tile_p, int tile_s, int cost_mult, int64_t max_items,
+                     const WsRegion& R) {
   SchedArgs a;
   a.cu_p = cu_p;
   a.cu_s = cu_s;
@@ -89,16 +99,18 @@ SchedArgs sched_args(void* ws, int64_t ws_bytes_needed, const int32_t* cu_p, con
   a.cost_mult = cost_mult;
   a.max_items = (int32_t)max_items;
   char* base = (char*)ws;
-  a.hdr = (WsHeader*)(base + L.hdr);
-  a.items = (WorkItem*)(base + L.items);
-  a.order = (int32_t*)(base + L.order);
-  a.seq_base = (int32_t*)(base + L.seq_base);
+  a.hdr = (WsHeader*)(base + R.hdr);
+  a.items = (WorkItem*)(base + R.items);
+  a.order = (int32_t*)(base + R.order);
+  a.seq_base = (int32_t*)(base + R.seq_base);
   return a;
 }
 
 }  // namespace
 
 CPATTN_API const char* cpattn_version(void) { return "cpattn 0.1 (gfx950)"; }
+
+CPATTN_API const char* cpattn_last_hip_error(void) { return g_last_hip_error; }
 
 CPATTN_API const char* cpattn_status_string(cpattn_status s) {
   switch (s) {
@@ -170,6 +182,7 @@ static cpattn_status partition_common(const cpattn_tensor* src, cpattn_tensor* d
   a.cp = cp;
   a.rank = rank;
   a.scatter = scatter ? 1 : 0;
+  clear_stale_error();
   return hip_status(launch_partition(a, (hipStream_t)stream));
 }
 
@@ -219,9 +232,10 @@ CPATTN_API size_t cpattn_workspace_size(int64_t tokens_q, int64_t tokens_k, int3
 
 CPATTN_API cpattn_status cpattn_workspace_status(const void* ws, void* stream, cpattn_status* out) {
   if (!ws || !out) return CPATTN_ERR_INVALID_ARG;
-  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return CPATTN_ERR_HIP;
+  cpattn_status st;
+  if ((st = hip_status(hipStreamSynchronize((hipStream_t)stream))) != CPATTN_OK) return st;
   int32_t v = 0;
-  if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return CPATTN_ERR_HIP;
+  if ((st = hip_status(hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost))) != CPATTN_OK) return st;
   *out = (cpattn_status)v;
   return CPATTN_OK;
 }
@@ -249,9 +263,10 @@ CPATTN_API cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_te
   const int d = q->head_dim;
   const int tile_p = fwd_tile_rows(bf16);
   const int64_t max_items = max_items_for(q->tokens, nseq, tile_p);
-  const SchedArgs sa = sched_args(ws, L.total, cu_q, cu_k, nseq, q->tokens, k->tokens, step, step->rank,
-                                  src_rank(step), true, mode, tile_p, 64, 1, max_items, L);
+  const SchedArgs sa = sched_args(ws, cu_q, cu_k, nseq, q->tokens, k->tokens, step, step->rank, src_rank(step),
+                                  true, mode, tile_p, 64, 1, max_items, L.a);
   hipStream_t s = (hipStream_t)stream;
+  clear_stale_error();
   if ((st = hip_status(launch_sched(sa, s))) != CPATTN_OK) return st;
   if (nseq == 0 || q->tokens == 0) return CPATTN_OK;
 
@@ -297,6 +312,7 @@ CPATTN_API cpattn_status cpattn_merge(float* out, float* lse, const cpattn_tenso
   a.heads = op->heads;
   a.d = op->head_dim;
   a.bf16 = op->dtype == CPATTN_BF16;
+  clear_stale_error();
   return hip_status(launch_merge(a, (hipStream_t)stream));
 }
 
@@ -315,6 +331,7 @@ CPATTN_API cpattn_status cpattn_bwd_preprocess(const float* out, const cpattn_te
   a.heads = dout->heads;
   a.d = dout->head_dim;
   a.bf16 = dout->dtype == CPATTN_BF16;
+  clear_stale_error();
   return hip_status(launch_delta(a, (hipStream_t)stream));
 }
 
@@ -356,22 +373,20 @@ CPATTN_API cpattn_status cpattn_bwd_step(const cpattn_tensor* q, const cpattn_te
   a.scale = sc; a.scale_log2 = sc * 1.4426950408889634f;
   a.mask = (int)mode;
 
-  // dQ: query tiles against the step's keys
-  const int tq = bwd_dq_tile_rows(bf16);
-  const int64_t mq = max_items_for(q->tokens, nseq, tq);
-  SchedArgs sq = sched_args(ws, L.total, cu_q, cu_k, nseq, q->tokens, k->tokens, step, step->rank,
-                            src_rank(step), true, mode, tq, 64, 1, mq, L);
+  // schedules: query tiles (dQ) in region A, key tiles (dK, dV; cost counts
+  // every q-head of the group) in region B
+  const int tq = bwd_dq_tile_rows(bf16), tk = bwd_dkv_tile_rows(bf16);
+  const int64_t mq = max_items_for(q->tokens, nseq, tq), mk = max_items_for(k->tokens, nseq, tk);
+  const SchedArgs sq = sched_args(ws, cu_q, cu_k, nseq, q->tokens, k->tokens, step, step->rank, src_rank(step),
+                                  true, mode, tq, 64, 1, mq, L.a);
+  const SchedArgs sk = sched_args(ws, cu_k, cu_q, nseq, k->tokens, q->tokens, step, src_rank(step), step->rank,
+                                  false, mode, tk, 64, grp, mk, L.b);
   a.tf_b = sq.tf_b; a.tf_n = sq.tf_n;
-  a.hdr = sq.hdr; a.items = sq.items; a.order = sq.order;
+  a.hdr_q = sq.hdr; a.items_q = sq.items; a.order_q = sq.order;
+  a.hdr_k = sk.hdr; a.items_k = sk.items; a.order_k = sk.order;
+  clear_stale_error();
   if ((st = hip_status(launch_sched(sq, s))) != CPATTN_OK) return st;
-  if (nseq > 0 && q->tokens > 0 && (st = hip_status(launch_bwd_dq(a, bf16, d, mq, s))) != CPATTN_OK) return st;
-
-  // dK, dV: key tiles against the rank's queries (all q-heads of a group)
-  const int tk = bwd_dkv_tile_rows(bf16);
-  const int64_t mk = max_items_for(k->tokens, nseq, tk);
-  SchedArgs sk = sched_args(ws, L.total, cu_k, cu_q, nseq, k->tokens, q->tokens, step, src_rank(step),
-                            step->rank, false, mode, tk, 64, grp, mk, L);
   if ((st = hip_status(launch_sched(sk, s))) != CPATTN_OK) return st;
-  if (nseq > 0 && k->tokens > 0) return hip_status(launch_bwd_dkv(a, bf16, d, mk, s));
-  return CPATTN_OK;
+  if (nseq == 0 || q->tokens == 0 || k->tokens == 0) return CPATTN_OK;
+  return hip_status(launch_bwd(a, bf16, d, mq, mk, s));
 }

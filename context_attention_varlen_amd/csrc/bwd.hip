@@ -10,7 +10,8 @@
 // splitting must not change the loss) needs exactly these per-step pieces;
 // the ring returns dK/dV of step s to their owner.
 //
-// Two kernels, no atomics, deterministic:
+// One kernel launch per step with two kinds of workgroups, no atomics,
+// deterministic:
 //   dkv  one workgroup per (128-key tile, kv-head): 4 waves x 32 keys hold
 //        K and V as MFMA operands and dK^T, dV^T accumulators in registers,
 //        and sweep every q-head of the GQA group and every query tile that
@@ -37,16 +38,16 @@ constexpr int kBwdBK = 64;                         // key rows per LDS tile (dq)
 // dq kernel (bf16)
 // ---------------------------------------------------------------------------
 template <int D, int NW, int QB>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, uint16_t* smem) {
   constexpr int BN = kBwdBK;
   constexpr int QW = 32 * QB;
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][BN * D];
+  uint16_t (*s_k)[BN * D] = (uint16_t (*)[BN * D])smem;
+  uint16_t (*s_v)[BN * D] = (uint16_t (*)[BN * D])(smem + 2 * BN * D);
 
   int item_rank, h, g;
-  map_block(blockIdx.x, a.grp, a.hkv, item_rank, h, g);
-  if (item_rank >= a.hdr->n_items) return;
-  const WorkItem it = a.items[a.order[item_rank]];
+  map_block(bid, a.grp, a.hkv, item_rank, h, g);
+  if (item_rank >= a.hdr_q->n_items) return;
+  const WorkItem it = a.items_q[a.order_q[item_rank]];
   if (it.nseg == 0) return;
 
   const int tid = threadIdx.x;
@@ -187,17 +188,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_bf16_kernel(BwdArgs a) {
 // dkv kernel (bf16)
 // ---------------------------------------------------------------------------
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dkv_bf16_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t* smem) {
   constexpr int BQ = kBwdBQ;
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_do[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) float s_lse[2][BQ];
-  __shared__ __attribute__((aligned(16))) float s_dl[2][BQ];
+  uint16_t (*s_q)[BQ * D] = (uint16_t (*)[BQ * D])smem;
+  uint16_t (*s_do)[BQ * D] = (uint16_t (*)[BQ * D])(smem + 2 * BQ * D);
+  float (*s_lse)[BQ] = (float (*)[BQ])(smem + 4 * BQ * D);
+  float (*s_dl)[BQ] = (float (*)[BQ])(smem + 4 * BQ * D + 4 * BQ);
 
   int item_rank, hdummy, g;
-  map_block(blockIdx.x, 1, a.hkv, item_rank, hdummy, g);
-  if (item_rank >= a.hdr->n_items) return;
-  const WorkItem it = a.items[a.order[item_rank]];
+  map_block(bid, 1, a.hkv, item_rank, hdummy, g);
+  if (item_rank >= a.hdr_k->n_items) return;
+  const WorkItem it = a.items_k[a.order_k[item_rank]];
   if (it.nseg == 0) return;
 
   const int tid = threadIdx.x;
@@ -342,6 +343,20 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkv_bf16_kernel(BwdArgs a) {
     }
 }
 
+// One launch per step: workgroups [0, dkv_blocks) take key tiles (the longer
+// items, dispatched first), the rest take query tiles.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_bf16_kernel(BwdArgs a) {
+  constexpr int DQ_LDS = 4 * kBwdBK * D;                 // 2 x (K, V) tiles
+  constexpr int DKV_LDS = 4 * kBwdBQ * D + 8 * kBwdBQ;   // 2 x (Q, dO) tiles + lse, delta
+  constexpr int LDS = DQ_LDS > DKV_LDS ? DQ_LDS : DKV_LDS;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[LDS];
+  static_assert(kDqWaves == 4 && kDkvWaves == 4, "both bodies run 256 threads");
+  const int bid = blockIdx.x;
+  if (bid < a.dkv_blocks) bwd_dkv_body<D, kDkvWaves>(a, bid, smem);
+  else bwd_dq_body<D, kDqWaves, kDqQB>(a, bid - a.dkv_blocks, smem);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 path: one row per thread.
 // ---------------------------------------------------------------------------
@@ -349,8 +364,8 @@ template <int D>
 __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdArgs a) {
   int item_rank, h, g;
   map_block(blockIdx.x, a.grp, a.hkv, item_rank, h, g);
-  if (item_rank >= a.hdr->n_items) return;
-  const WorkItem it = a.items[a.order[item_rank]];
+  if (item_rank >= a.hdr_q->n_items) return;
+  const WorkItem it = a.items_q[a.order_q[item_rank]];
   const int r = threadIdx.x;
   if (r >= it.nrows) return;
   const int64_t row = it.row0 + r;
@@ -387,8 +402,8 @@ template <int D>
 __global__ __launch_bounds__(64) void bwd_dkv_f32_kernel(BwdArgs a) {
   int item_rank, hdummy, g;
   map_block(blockIdx.x, 1, a.hkv, item_rank, hdummy, g);
-  if (item_rank >= a.hdr->n_items) return;
-  const WorkItem it = a.items[a.order[item_rank]];
+  if (item_rank >= a.hdr_k->n_items) return;
+  const WorkItem it = a.items_k[a.order_k[item_rank]];
   const int r = threadIdx.x;
   if (r >= it.nrows) return;
   const int64_t row = it.row0 + r;
@@ -430,26 +445,23 @@ __global__ __launch_bounds__(64) void bwd_dkv_f32_kernel(BwdArgs a) {
 int bwd_dq_tile_rows(bool bf16) { return bf16 ? 32 * kDqQB * kDqWaves : 64; }
 int bwd_dkv_tile_rows(bool bf16) { return bf16 ? 32 * kDkvWaves : 64; }
 
-hipError_t launch_bwd_dq(const BwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream) {
-  const dim3 grid(unit_grid(max_items, a.hkv, a.grp));
+hipError_t launch_bwd(BwdArgs a, bool bf16, int d, int64_t max_items_q, int64_t max_items_k, hipStream_t stream) {
+  const unsigned gq = unit_grid(max_items_q, a.hkv, a.grp);
+  const unsigned gk = unit_grid(max_items_k, a.hkv, 1);
   if (bf16) {
-    if (d == 128) hipLaunchKernelGGL((bwd_dq_bf16_kernel<128, kDqWaves, kDqQB>), grid, dim3(64 * kDqWaves), 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dq_bf16_kernel<64, kDqWaves, kDqQB>), grid, dim3(64 * kDqWaves), 0, stream, a);
+    a.dkv_blocks = (int)gk;
+    const dim3 grid(gk + gq);
+    if (d == 128) hipLaunchKernelGGL(bwd_bf16_kernel<128>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(bwd_bf16_kernel<64>, grid, dim3(256), 0, stream, a);
   } else {
-    if (d == 128) hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, grid, dim3(64), 0, stream, a);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_dkv(const BwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream) {
-  const dim3 grid(unit_grid(max_items, a.hkv, 1));
-  if (bf16) {
-    if (d == 128) hipLaunchKernelGGL((bwd_dkv_bf16_kernel<128, kDkvWaves>), grid, dim3(64 * kDkvWaves), 0, stream, a);
-    else hipLaunchKernelGGL((bwd_dkv_bf16_kernel<64, kDkvWaves>), grid, dim3(64 * kDkvWaves), 0, stream, a);
-  } else {
-    if (d == 128) hipLaunchKernelGGL(bwd_dkv_f32_kernel<128>, grid, dim3(64), 0, stream, a);
-    else hipLaunchKernelGGL(bwd_dkv_f32_kernel<64>, grid, dim3(64), 0, stream, a);
+    a.dkv_blocks = 0;
+    if (d == 128) {
+      hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, dim3(gq), dim3(64), 0, stream, a);
+      hipLaunchKernelGGL(bwd_dkv_f32_kernel<128>, dim3(gk), dim3(64), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, dim3(gq), dim3(64), 0, stream, a);
+      hipLaunchKernelGGL(bwd_dkv_f32_kernel<64>, dim3(gk), dim3(64), 0, stream, a);
+    }
   }
   return hipGetLastError();
 }

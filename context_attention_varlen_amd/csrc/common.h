@@ -67,9 +67,15 @@ struct SchedArgs {
   int32_t* seq_base;     // [nseq + 1] first item of every sequence
 };
 
-// Workspace carve-up shared by host code.
+// Workspace carve-up shared by host code: two schedule regions (A: query
+// tiles, used by the forward and the dQ pass; B: key tiles, used by the
+// dK/dV pass), each with a header, items, sorted order and per-sequence base.
+struct WsRegion {
+  size_t hdr, items, order, seq_base, end;
+};
 struct WsLayout {
-  size_t hdr, items, order, seq_base, total;
+  WsRegion a, b;
+  size_t total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -81,15 +87,22 @@ inline int64_t max_items_for(int64_t tokens, int32_t nseq, int tile) {
   return (tokens + tile - 1) / tile + 2 * (int64_t)nseq + 1;
 }
 
+inline WsRegion ws_region(size_t base, int64_t tokens, int32_t nseq) {
+  const int64_t mi = max_items_for(tokens, nseq, kMinTile);
+  WsRegion r;
+  r.hdr = base;
+  r.items = base + 256;
+  r.order = align_up(r.items + mi * sizeof(WorkItem), 256);
+  r.seq_base = align_up(r.order + mi * sizeof(int32_t), 256);
+  r.end = align_up(r.seq_base + (nseq + 1) * sizeof(int32_t), 256);
+  return r;
+}
+
 inline WsLayout ws_layout(int64_t tokens_q, int64_t tokens_k, int32_t nseq) {
-  int64_t tmax = tokens_q > tokens_k ? tokens_q : tokens_k;
-  int64_t mi = max_items_for(tmax, nseq, kMinTile);
   WsLayout L;
-  L.hdr = 0;
-  L.items = 256;
-  L.order = align_up(L.items + mi * sizeof(WorkItem), 256);
-  L.seq_base = align_up(L.order + mi * sizeof(int32_t), 256);
-  L.total = align_up(L.seq_base + (nseq + 1) * sizeof(int32_t), 256);
+  L.a = ws_region(0, tokens_q, nseq);
+  L.b = ws_region(L.a.end, tokens_k, nseq);
+  L.total = L.b.end;
   return L;
 }
 
@@ -126,9 +139,13 @@ struct BwdArgs {
   int hq, hkv, grp;
   float scale, scale_log2;
   int mask, tf_b, tf_n;
-  const WsHeader* hdr;
-  const WorkItem* items;
-  const int32_t* order;
+  const WsHeader* hdr_q;     // query-tile schedule (dQ)
+  const WorkItem* items_q;
+  const int32_t* order_q;
+  const WsHeader* hdr_k;     // key-tile schedule (dK, dV)
+  const WorkItem* items_k;
+  const int32_t* order_k;
+  int dkv_blocks;            // workgroups [0, dkv_blocks) run dK/dV tiles
 };
 
 struct MergeArgs {
@@ -173,8 +190,7 @@ hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, int64_t max_items, hip
 int fwd_tile_rows(bool bf16);
 int bwd_dq_tile_rows(bool bf16);
 int bwd_dkv_tile_rows(bool bf16);
-hipError_t launch_bwd_dq(const BwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream);
-hipError_t launch_bwd_dkv(const BwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream);
+hipError_t launch_bwd(BwdArgs a, bool bf16, int d, int64_t max_items_q, int64_t max_items_k, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_delta(const DeltaArgs& a, hipStream_t stream);
 hipError_t launch_partition(const PartArgs& a, hipStream_t stream);

@@ -114,6 +114,10 @@ typedef struct {
 const char* cpattn_version(void);
 const char* cpattn_status_string(cpattn_status s);
 
+/* Text of the HIP error behind the last CPATTN_ERR_HIP returned on the
+ * calling thread ("" if none).  Valid until the next call on that thread. */
+const char* cpattn_last_hip_error(void);
+
 /* ---- zigzag partition -----------------------------------------------------
  * Zigzag split (LongVILA article, ZIGZAG-RINGATTN; the chunk rule is not
  * printed there, this is the reading that balances causal work exactly):

@@ -1,0 +1,191 @@
+"""Full-size workloads through the C ABI, in the launch configuration bench.py
+times, checked against the fp64 oracle on seeded samples of rows (the oracle
+computes each sampled row against every key it may attend) and, for the
+backward, with invariants that hold at any size."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+from tests._gpu import TOL_GRAD_RELRMS, check_lse, check_out, rel_rms, tdtype  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def cpa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import context_attention_varlen_amd as c
+    return c
+
+
+def _seq_pos(cu):
+    T = int(cu[-1])
+    seq = np.repeat(np.arange(len(cu) - 1), np.diff(cu))
+    return seq, np.arange(T) - np.asarray(cu)[seq]
+
+
+def _sample_local_rows(w, r, count, seed):
+    """Stratified seeded sample of a rank's local rows: first/last row of every
+    local chunk, rows next to 64/128/256 tile edges, plus uniform rows."""
+    cu_l, l2g, _, _ = oracle.local_rows(w.cu_seqlens, w.cp, r)
+    edges = []
+    for b in range(len(cu_l) - 1):
+        n = cu_l[b + 1] - cu_l[b]
+        halves = [(cu_l[b], n)] if w.cp == 1 else [(cu_l[b], n // 2), (cu_l[b] + n // 2, n // 2)]
+        for s0, m in halves:
+            if m == 0:
+                continue
+            edges += [s0, s0 + m - 1]
+            for t in (64, 128, 256):
+                if m > t:
+                    edges += [s0 + t - 1, s0 + t]
+    rng = np.random.default_rng(1000 + r)
+    base = workloads.sample_rows(rng, len(l2g), count)
+    edges = np.unique(np.asarray(edges))
+    extra = rng.choice(edges, size=min(len(edges), count), replace=False) if len(edges) else []
+    return np.unique(np.concatenate([base, np.asarray(extra, dtype=np.int64)]))
+
+
+def _oracle_rows(w, x, r, rows, step=None):
+    """Oracle output/LSE of a rank's sampled local rows: against every key of
+    their sequence (merged result) or only the keys of one ring step."""
+    _, l2g, qpos, qseq = oracle.local_rows(w.cu_seqlens, w.cp, r)
+    if step is None:
+        seq, pos = _seq_pos(w.cu_seqlens)
+        kidx = np.nonzero(np.isin(seq, np.unique(qseq[rows])))[0]
+        kseq, kpos = seq[kidx], pos[kidx]
+    else:
+        _, kidx, kpos, kseq = oracle.local_rows(w.cu_seqlens, w.cp, oracle.step_source(w.cp, r, step))
+    return oracle.attention(x["q"][l2g[rows]], x["k"][kidx], x["v"][kidx], qseq[rows], qpos[rows], kseq, kpos,
+                            w.mask, tf_chunk=w.tf_chunk, tf_num=w.tf_num)
+
+
+def _gpu_ring(w, x, r, keep=False, backward=False):
+    from context_attention_varlen_amd.ring import RankPlan, partition, ring_backward, ring_forward
+    td = tdtype(w.dtype)
+    plan = RankPlan.make(w.cu_seqlens, w.cp, r)
+    q = partition(torch.from_numpy(x["q"]).to(td).cuda(), plan)
+    kg = torch.from_numpy(x["k"]).to(td).cuda()
+    vg = torch.from_numpy(x["v"]).to(td).cuda()
+    ks = [partition(kg, plan, j) for j in range(w.cp)]
+    vs = [partition(vg, plan, j) for j in range(w.cp)]
+    del kg, vg
+    torch.cuda.empty_cache()
+    tf = (w.tf_chunk, w.tf_num)
+    bufs, parts = ring_forward(q, ks, vs, plan, w.mask, tf=tf, keep_partials=keep)
+    grads = None
+    if backward:
+        do = partition(torch.from_numpy(x["dout"]).to(td).cuda(), plan)
+        grads = ring_backward(q, ks, vs, do, bufs, plan, w.mask, tf=tf)
+    torch.cuda.synchronize()
+    return plan, bufs, parts, grads
+
+
+@pytest.fixture(scope="module")
+def long_video_inputs():
+    return workloads.draw(workloads.WORKLOADS["long_video"])
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_long_video_rank(cpa, long_video_inputs, rank):
+    """262144 tokens, cp=8 zigzag, 28/4 heads: all 8 forward steps and merges
+    of one rank; sampled rows of the merged result and of two step partials."""
+    w = workloads.WORKLOADS["long_video"]
+    x = long_video_inputs
+    plan, bufs, parts, _ = _gpu_ring(w, x, rank, keep=True)
+    rows = _sample_local_rows(w, rank, 48, 0)
+    o_ref, l_ref = _oracle_rows(w, x, rank, rows)
+    t = torch.from_numpy(rows).cuda()
+    check_out(bufs.out[t].cpu().numpy(), o_ref, "bf16")
+    check_lse(bufs.lse[:, t].cpu().numpy(), l_ref)
+    for s in (0, 1, 7):
+        o_ref, l_ref = _oracle_rows(w, x, rank, rows, step=s)
+        op, lp = parts[s]
+        check_out(op[t].float().cpu().numpy(), o_ref, "bf16")
+        check_lse(lp[:, t].cpu().numpy(), l_ref)
+    # balance of the zigzag split: the exact pair count is rank-independent
+    assert sum(cpa.cpattn_count_pairs(w.cu_seqlens, w.mask, cpa.make_step(8, rank, s)) for s in range(8)) \
+        == 4_294_983_680
+
+
+def test_tf_dit_sampled(cpa):
+    """Teacher-forced DiT, 74880 tokens, block mask: sampled rows stratified
+    over both streams and the chunk edges (B = 3120 is not a tile multiple)."""
+    w = workloads.WORKLOADS["tf_dit"]
+    x = workloads.draw(w)
+    plan, bufs, _, _ = _gpu_ring(w, x, 0)
+    B, N = w.tf_chunk, w.tf_num
+    edges = []
+    for c in range(2 * N):
+        edges += [c * B, c * B + 1, c * B + B - 1]
+    rng = np.random.default_rng(1003)
+    rows = workloads.sample_rows(rng, w.tokens, 40, edges)
+    o_ref, l_ref = _oracle_rows(w, x, 0, rows)
+    t = torch.from_numpy(rows).cuda()
+    check_out(bufs.out[t].cpu().numpy(), o_ref, "bf16")
+    check_lse(bufs.lse[:, t].cpu().numpy(), l_ref)
+
+
+def test_long_tail_forward_backward(cpa):
+    """65536 tokens (49152 + 15 short), cp=4 zigzag, 32/8 heads, rank 0:
+    sampled forward rows; dQ on sampled query rows; dK/dV on sampled key rows
+    whose attending queries the oracle can enumerate (every short-sequence key
+    and the last keys of the long sequence); sum invariants over all keys."""
+    w = workloads.WORKLOADS["long_tail"]
+    x = workloads.draw(w)
+    r = 0
+    plan, bufs, _, grads = _gpu_ring(w, x, r, backward=True)
+    dq, dk, dv, _ = grads
+    cu = w.cu_seqlens
+    cu_l, l2g, qpos, qseq = oracle.local_rows(cu, w.cp, r)
+    seq, pos = _seq_pos(cu)
+
+    # forward and dQ on sampled rows
+    rows = _sample_local_rows(w, r, 40, 0)
+    o_ref, l_ref = _oracle_rows(w, x, r, rows)
+    t = torch.from_numpy(rows).cuda()
+    check_out(bufs.out[t].cpu().numpy(), o_ref, "bf16")
+    check_lse(bufs.lse[:, t].cpu().numpy(), l_ref)
+    kidx = np.nonzero(np.isin(seq, np.unique(qseq[rows])))[0]
+    delta = oracle.bwd_delta(o_ref, x["dout"][l2g[rows]])
+    dq_ref, _, _ = oracle.attention_backward(x["q"][l2g[rows]], x["k"][kidx], x["v"][kidx], x["dout"][l2g[rows]],
+                                             l_ref, delta, qseq[rows], qpos[rows], seq[kidx], pos[kidx], w.mask)
+    assert rel_rms(dq[t].cpu().numpy(), dq_ref) <= TOL_GRAD_RELRMS
+
+    # dK/dV on keys of three short sequences (all of their rank-0 queries)
+    # and on the last 128 keys of the long sequence (its queries at the end)
+    for b, key_filter in ((1, None), (7, None), (15, None), (0, lambda p: p >= 49152 - 128)):
+        qrows = np.nonzero(qseq == b)[0]
+        if key_filter is not None:
+            qrows = qrows[qpos[qrows] >= 49152 - 128]
+        o_b, l_b = _oracle_rows(w, x, r, qrows)
+        d_b = oracle.bwd_delta(o_b, x["dout"][l2g[qrows]])
+        for s in range(w.cp):
+            j = oracle.step_source(w.cp, r, s)
+            _, k2g, kpos, kseq = oracle.local_rows(cu, w.cp, j)
+            ksel = np.nonzero(kseq == b)[0]
+            if key_filter is not None:
+                ksel = ksel[key_filter(kpos[ksel])]
+            if len(ksel) == 0:
+                continue
+            _, dk_ref, dv_ref = oracle.attention_backward(
+                x["q"][l2g[qrows]], x["k"][k2g[ksel]], x["v"][k2g[ksel]], x["dout"][l2g[qrows]], l_b, d_b,
+                qseq[qrows], qpos[qrows], kseq[ksel], kpos[ksel], w.mask)
+            kt = torch.from_numpy(ksel).cuda()
+            assert rel_rms(dk[j][kt].cpu().numpy(), dk_ref) <= TOL_GRAD_RELRMS, (b, j)
+            assert rel_rms(dv[j][kt].cpu().numpy(), dv_ref) <= TOL_GRAD_RELRMS, (b, j)
+
+    # invariants over every key: sum_j dV_j = sum_i dO_i, sum_j dK_j = 0
+    do_loc = torch.from_numpy(x["dout"][l2g]).cuda()
+    grp = w.heads_q // w.heads_kv
+    for b in range(len(w.seqlens)):
+        rs = slice(int(cu_l[b]), int(cu_l[b + 1]))
+        dv_sum = sum(dv[j][rs].double().sum(0) for j in range(w.cp))
+        dk_sum = sum(dk[j][rs].double().sum(0) for j in range(w.cp))
+        want = do_loc[rs].double().sum(0).view(w.heads_kv, grp, w.head_dim).sum(1)
+        scale = float(do_loc[rs].double().norm()) / np.sqrt(w.head_dim * w.heads_kv)
+        assert float((dv_sum - want).abs().max()) <= 1e-2 * max(1.0, scale), b
+        assert float(dk_sum.abs().max()) <= 1e-2 * max(1.0, scale), b
