@@ -20,6 +20,9 @@ HIPCC_FLAGS = [
     # never emit packed fp32 VALU ops (v_pk_{add,mul,fma}_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # keep MFMA accumulators in VGPRs: the softmax reads every score element
+    # with VALU ops, and AGPR-resident scores cost a v_accvgpr_read each
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

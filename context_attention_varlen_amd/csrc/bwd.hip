@@ -13,25 +13,28 @@
 // One kernel launch per step with two kinds of workgroups, no atomics,
 // deterministic:
 //   dkv  one workgroup per (128-key tile, kv-head): 4 waves x 32 keys hold
-//        K and V as MFMA operands and dK^T, dV^T accumulators in registers,
-//        and sweep every q-head of the GQA group and every query tile that
-//        can see the keys (64 rows, Q/dO tiles in LDS, double-buffered):
-//          S = Q K^T, dP = dO V^T               (row reads of Q, dO)
+//        K as an MFMA operand and dK^T, dV^T accumulators in registers (V's
+//        operand rows are read from an LDS copy of the key tile), and sweep
+//        every q-head of the GQA group and every query tile that can see the
+//        keys (32 rows, Q/dO tiles in LDS, double-buffered):
+//          S = Q K^T, dP = dO V^T               (row reads of Q, dO, V)
 //          dV^T += dO^T P, dK^T += Q^T dS       (transposing reads of dO, Q)
-//   dq   one workgroup per (256-query tile, q-head): 4 waves x 64 queries
+//   dq   one workgroup per (128-query tile, q-head): 4 waves x 32 queries
 //        hold Q, dO operands and dQ^T accumulators, sweeping key tiles:
 //          S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T
 // Each accumulator element is owned by one workgroup, so += is a plain
-// read-modify-write.  The fp32 path uses plain per-row kernels.
+// read-modify-write.  Both kinds fit 256 registers per wave and ~65 KiB of
+// LDS, so the kernel runs two waves per SIMD (two workgroups per CU).  The
+// fp32 path uses plain per-row kernels.
 #include "mfma.h"
 
 namespace cpattn {
 
 namespace {
 
-constexpr int kDqWaves = 4, kDqQB = 2;            // dq: 4 waves x 64 queries
+constexpr int kDqWaves = 4, kDqQB = 1;            // dq: 4 waves x 32 queries
 constexpr int kDkvWaves = 4;                       // dkv: 4 waves x 32 keys
-constexpr int kBwdBQ = 64;                         // query rows per LDS tile (dkv)
+constexpr int kBwdBQ = 32;                         // query rows per LDS tile (dkv)
 constexpr int kBwdBK = 64;                         // key rows per LDS tile (dq)
 
 // ---------------------------------------------------------------------------
@@ -140,8 +143,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, uint16_t*
           const int off = 8 * (i >> 2) + (i & 3);
           const bool in = off < rem;
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            if (!(in && in_ranges(kr[qb], pbase + off))) st[qb][i] = -INFINITY;
+          for (int qb = 0; qb < QB; ++qb) {
+            const bool ok = in & in_ranges(kr[qb], pbase + off);
+            st[qb][i] = ok ? st[qb][i] : -INFINITY;
+          }
         }
       }
       bf16x8 dsb[QB][2];
@@ -189,11 +194,13 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, uint16_t*
 // ---------------------------------------------------------------------------
 template <int D, int NW>
 __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t* smem) {
-  constexpr int BQ = kBwdBQ;
-  uint16_t (*s_q)[BQ * D] = (uint16_t (*)[BQ * D])smem;
-  uint16_t (*s_do)[BQ * D] = (uint16_t (*)[BQ * D])(smem + 2 * BQ * D);
-  float (*s_lse)[BQ] = (float (*)[BQ])(smem + 4 * BQ * D);
-  float (*s_dl)[BQ] = (float (*)[BQ])(smem + 4 * BQ * D + 4 * BQ);
+  constexpr int BQ = kBwdBQ;                 // query rows per LDS tile (one 32-row MFMA block)
+  constexpr int BK = 32 * NW;                // keys per workgroup
+  uint16_t* s_v = smem;                                                   // [BK][D], loaded once
+  uint16_t (*s_q)[BQ * D] = (uint16_t (*)[BQ * D])(smem + BK * D);       // [2][BQ][D]
+  uint16_t (*s_do)[BQ * D] = (uint16_t (*)[BQ * D])(smem + BK * D + 2 * BQ * D);
+  float (*s_lse)[64] = (float (*)[64])(smem + BK * D + 4 * BQ * D);      // [2][64]
+  float (*s_dl)[64] = (float (*)[64])(smem + BK * D + 4 * BQ * D + 256);
 
   int item_rank, hdummy, g;
   map_block(bid, 1, a.hkv, item_rank, hdummy, g);
@@ -208,21 +215,18 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
   const bool key_ok = kr_ < it.nrows;
   const KeyRanges qrng = query_ranges(a.mask, it.pos0 + kr_, a.tf_b, a.tf_n);
 
-  // K, V as B operands (B[k = d][n = key]): lane holds X[key][16*ks + 8*hh + 0..7]
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // V rows of the whole key tile go to LDS once (B operand of dP = dO V^T
+  // is read from there); K stays in registers as the B operand of S = Q K^T:
+  // lane holds K[key][16*ks + 8*hh + 0..7].
+  load_tile<D, BK, NW>(s_v, (const uint16_t*)a.v + (int64_t)g * a.v_sh, a.v_st, it.row0, 0, it.nrows, wave, lane);
+  bf16x8 kreg[D / 16];
   {
-    const int64_t row = it.row0 + kr_;
-    const uint16_t* ks_ = (const uint16_t*)a.k + row * a.k_st + (int64_t)g * a.k_sh + 8 * hh;
-    const uint16_t* vs_ = (const uint16_t*)a.v + row * a.v_st + (int64_t)g * a.v_sh + 8 * hh;
+    const uint16_t* ks_ = (const uint16_t*)a.k + (int64_t)(it.row0 + kr_) * a.k_st + (int64_t)g * a.k_sh + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
-      if (key_ok) {
-        rk = *(const u32x4*)(ks_ + 16 * ks);
-        rv = *(const u32x4*)(vs_ + 16 * ks);
-      }
+      u32x4 rk = {0u, 0u, 0u, 0u};
+      if (key_ok) rk = *(const u32x4*)(ks_ + 16 * ks);
       kreg[ks] = __builtin_bit_cast(bf16x8, rk);
-      vreg[ks] = __builtin_bit_cast(bf16x8, rv);
     }
   }
 
@@ -267,60 +271,54 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
     if (j + 1 < ntiles) issue(j + 1);
     int h, s, t0;
     tile_of(j, h, s, t0);
+    (void)h;
     const Segment sg = it.seg[s];
     const uint16_t* tq = s_q[buf];
     const uint16_t* tdo = s_do[buf];
     const bool full = t0 >= sg.full_lo && t0 + BQ <= sg.full_hi;
+
+    // S = Q K^T and dP = dO V^T for the tile's 32 query rows x this wave's 32 keys
+    f32x16 st, dp;
 #pragma unroll
-    for (int qb = 0; qb < BQ / 32; ++qb) {
-      // S = Q K^T and dP = dO V^T for 32 query rows x this wave's 32 keys
-      f32x16 st, dp;
+    for (int i = 0; i < 16; ++i) { st[i] = 0.f; dp[i] = 0.f; }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { st[i] = 0.f; dp[i] = 0.f; }
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 aq = read_row8<D>(tq, col, 2 * ks + hh);
+      const bf16x8 ad = read_row8<D>(tdo, col, 2 * ks + hh);
+      const bf16x8 bv = read_row8<D>(s_v, kr_, 2 * ks + hh);
+      st = mfma32(aq, kreg[ks], st);
+      dp = mfma32(ad, bv, dp);
+    }
+    // rows of this lane: q = 8*(i/4) + 4*hh + i%4
+    const int qofs0 = t0 + 4 * hh;
+    const int rem = sg.n - qofs0;
+    const int pbase = sg.pos + qofs0;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 aq = read_row8<D>(tq, qb * 32 + col, 2 * ks + hh);
-        const bf16x8 ad = read_row8<D>(tdo, qb * 32 + col, 2 * ks + hh);
-        st = mfma32(aq, kreg[ks], st);
-        dp = mfma32(ad, vreg[ks], dp);
-      }
-      // rows of this lane: q = qb*32 + 8*(i/4) + 4*hh + i%4
-      const int qb0 = qb * 32 + 4 * hh;
-      f32x4 l4[4], d4[4];
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 l4 = *(const f32x4*)(&s_lse[buf][4 * hh + 8 * i4]);
+      const f32x4 d4 = *(const f32x4*)(&s_dl[buf][4 * hh + 8 * i4]);
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        l4[i4] = *(const f32x4*)(&s_lse[buf][qb0 + 8 * i4]);
-        d4[i4] = *(const f32x4*)(&s_dl[buf][qb0 + 8 * i4]);
-      }
-      const int qofs0 = t0 + qb0;
-      const int rem = sg.n - qofs0;
-      const int pbase = sg.pos + qofs0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int off = 8 * (i >> 2) + (i & 3);
-        const float l = l4[i >> 2][i & 3];
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * i4 + e;
+        const int off = 8 * i4 + e;
+        const float l = l4[e];
         const float lse2 = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
         float p = __builtin_amdgcn_exp2f(st[i] * a.scale_log2 - lse2);
-        if (!full && !(off < rem && in_ranges(qrng, pbase + off))) p = 0.f;
+        const bool ok = full | ((off < rem) & in_ranges(qrng, pbase + off));
+        p = ok ? p : 0.f;
         st[i] = p;
-        dp[i] = p * (dp[i] - d4[i >> 2][i & 3]);
+        dp[i] = p * (dp[i] - d4[e]);
       }
-      bf16x8 pb[2], dsb[2];
-      pb[0] = pack_b(st, 0);
-      pb[1] = pack_b(st, 1);
-      dsb[0] = pack_b(dp, 0);
-      dsb[1] = pack_b(dp, 1);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const bf16x8 adt = read_tr<D>(tdo, 32 * qb + 16 * hs, 32 * db, lane);
-          const bf16x8 aqt = read_tr<D>(tq, 32 * qb + 16 * hs, 32 * db, lane);
-          acc_v[db] = mfma32(adt, pb[hs], acc_v[db]);
-          acc_k[db] = mfma32(aqt, dsb[hs], acc_k[db]);
-        }
     }
-    (void)h;
+    const bf16x8 pb0 = pack_b(st, 0), pb1 = pack_b(st, 1);
+    const bf16x8 ds0 = pack_b(dp, 0), ds1 = pack_b(dp, 1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      acc_v[db] = mfma32(read_tr<D>(tdo, 0, 32 * db, lane), pb0, acc_v[db]);
+      acc_v[db] = mfma32(read_tr<D>(tdo, 16, 32 * db, lane), pb1, acc_v[db]);
+      acc_k[db] = mfma32(read_tr<D>(tq, 0, 32 * db, lane), ds0, acc_k[db]);
+      acc_k[db] = mfma32(read_tr<D>(tq, 16, 32 * db, lane), ds1, acc_k[db]);
+    }
   }
 
   if (!key_ok) return;
@@ -346,9 +344,9 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
 // One launch per step: workgroups [0, dkv_blocks) take key tiles (the longer
 // items, dispatched first), the rest take query tiles.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_bf16_kernel(BwdArgs a) {
-  constexpr int DQ_LDS = 4 * kBwdBK * D;                 // 2 x (K, V) tiles
-  constexpr int DKV_LDS = 4 * kBwdBQ * D + 8 * kBwdBQ;   // 2 x (Q, dO) tiles + lse, delta
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_bf16_kernel(BwdArgs a) {
+  constexpr int DQ_LDS = 4 * kBwdBK * D;                            // 2 x (K, V) tiles
+  constexpr int DKV_LDS = 32 * kDkvWaves * D + 4 * kBwdBQ * D + 512; // V tile + 2 x (Q, dO) + lse, delta
   constexpr int LDS = DQ_LDS > DKV_LDS ? DQ_LDS : DKV_LDS;
   __shared__ __attribute__((aligned(16))) uint16_t smem[LDS];
   static_assert(kDqWaves == 4 && kDkvWaves == 4, "both bodies run 256 threads");

@@ -3,9 +3,14 @@
 // section 2, Ring Attention paragraph), with the online softmax that makes
 // a block's output and log-sum-exp exact for that block.
 //
-// bf16 path (gfx950 MFMA).  One workgroup = one tile of 256 query rows x one
-// q-head; 4 waves (one per SIMD), each owning 64 query rows as two 32-column
-// MFMA blocks that share every K operand read.  Per key tile of 64 rows:
+// bf16 path (gfx950 MFMA).  One workgroup = one tile of 128 query rows x one
+// q-head; 4 waves of 32 query rows each, compiled for two waves per SIMD
+// (two workgroups per CU, 64 KiB of LDS each), so that one wave's softmax
+// runs while the other's MFMAs do (with one wave per SIMD the MFMA drains,
+// cross-lane exchanges and barriers stall the SIMD).  The kernel is also
+// templated for 64 query rows per wave (two MFMA column blocks sharing every
+// K operand read); that form needs one wave per SIMD and measured slower.
+// Per key tile of 64 rows:
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K from LDS, Q in registers;
 //                    the transposed product puts one query per lane column,
 //                    so row statistics are in-lane plus one lane^32 swap.
@@ -34,8 +39,14 @@ namespace cpattn {
 // tiles.  O / l and m + log2(l) use the same m, so the result is exact.
 constexpr float kRescale = 8.0f;
 
+// Waves per SIMD the kernel is compiled for: two when each wave owns 32
+// queries (so one wave's softmax overlaps the other's MFMAs), else one.
+template <int QB>
+struct FwdOcc { static constexpr int value = QB == 1 ? 2 : 1; };
+
 template <int D, int NW, int QB>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FwdOcc<QB>::value, FwdOcc<QB>::value)))
+void fwd_bf16_kernel(FwdArgs a) {
   constexpr int BN = 64;
   constexpr int QW = 32 * QB;                 // query rows per wave
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][BN * D];
@@ -135,8 +146,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdArgs a) {
           const int off = 8 * (i >> 2) + (i & 3);
           const bool in = off < rem;
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            if (!(in && in_ranges(kr[qb], pbase + off))) acc_s[qb][i] = -INFINITY;
+          for (int qb = 0; qb < QB; ++qb) {
+            const bool ok = in & in_ranges(kr[qb], pbase + off);
+            acc_s[qb][i] = ok ? acc_s[qb][i] : -INFINITY;
+          }
         }
       }
 
@@ -261,9 +274,12 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
 }
 
 #ifndef CPATTN_FWD_QB
-#define CPATTN_FWD_QB 2
+#define CPATTN_FWD_QB 1
 #endif
-constexpr int kFwdWaves = 4, kFwdQB = CPATTN_FWD_QB;
+#ifndef CPATTN_FWD_WAVES
+#define CPATTN_FWD_WAVES 4
+#endif
+constexpr int kFwdWaves = CPATTN_FWD_WAVES, kFwdQB = CPATTN_FWD_QB;
 constexpr int kFwdTile = 32 * kFwdQB * kFwdWaves;
 
 int fwd_tile_rows(bool bf16) { return bf16 ? kFwdTile : 64; }
