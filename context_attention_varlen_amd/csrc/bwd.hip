@@ -26,6 +26,8 @@
 // read-modify-write.  Both kinds fit 256 registers per wave and ~65 KiB of
 // LDS, so the kernel runs two waves per SIMD (two workgroups per CU).  The
 // fp32 path uses plain per-row kernels.
+#include <type_traits>
+
 #include "mfma.h"
 
 namespace cpattn {
@@ -53,23 +55,28 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, uint16_t*
   const WorkItem it = a.items_q[a.order_q[item_rank]];
   if (it.nseg == 0) return;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int col = lane & 31, hh = lane >> 5;
-  const uint16_t* kbase = (const uint16_t*)a.k + (int64_t)g * a.k_sh;
-  const uint16_t* vbase = (const uint16_t*)a.v + (int64_t)g * a.v_sh;
+  const int64_t kst = a.k_st * 2, vst = a.v_st * 2;     // row strides in bytes
+  const char* kbase = (const char*)a.k + (int64_t)g * a.k_sh * 2;
+  const char* vbase = (const char*)a.v + (int64_t)g * a.v_sh * 2;
+  TileLoader<D, BN, NW> lk, lv;
+  lk.init(kst, wave, lane);
+  lv.init(vst, wave, lane);
 
   const int nt0 = ceil_div(it.seg[0].n, BN);
   const int nt1 = it.nseg > 1 ? ceil_div(it.seg[1].n, BN) : 0;
   const int ntiles = nt0 + nt1;
-  auto issue = [&](int j) {
+  auto issue = [&](int j, int buf) {
     const int s = j < nt0 ? 0 : 1;
     const int t0 = (j - (s ? nt0 : 0)) * BN;
     const Segment& sg = it.seg[s];
-    load_tile<D, BN, NW>(s_k[j & 1], kbase, a.k_st, sg.row, t0, sg.n, wave, lane);
-    load_tile<D, BN, NW>(s_v[j & 1], vbase, a.v_st, sg.row, t0, sg.n, wave, lane);
+    const int nvalid = min(BN, sg.n - t0);
+    const int64_t row = sg.row + t0;
+    lk.issue(s_k[buf], kbase + row * kst, nvalid, kst);
+    lv.issue(s_v[buf], vbase + row * vst, nvalid, vst);
   };
-  issue(0);
+  issue(0, 0);
 
   bf16x8 qreg[QB][D / 16], doreg[QB][D / 16];
   KeyRanges kr[QB];
@@ -106,11 +113,11 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, uint16_t*
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[qb][db][i] = 0.f;
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
+  auto tile = [&](int j, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     wait_loads();
     __syncthreads();
-    if (j + 1 < ntiles) issue(j + 1);
+    if (j + 1 < ntiles) issue(j + 1, buf ^ 1);
     const int s = j < nt0 ? 0 : 1;
     const int t0 = (j - (s ? nt0 : 0)) * BN;
     const Segment sg = it.seg[s];
@@ -169,6 +176,10 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, uint16_t*
           for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(akt, dsb[qb][hs], acc[qb][db]);
         }
     }
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(j, std::integral_constant<int, 0>{});
+    if (j + 1 < ntiles) tile(j + 1, std::integral_constant<int, 1>{});
   }
 
 #pragma unroll
@@ -208,8 +219,7 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
   const WorkItem it = a.items_k[a.order_k[item_rank]];
   if (it.nseg == 0) return;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int col = lane & 31, hh = lane >> 5;
   const int kr_ = wave * 32 + col;                  // key row in the tile
   const bool key_ok = kr_ < it.nrows;
@@ -218,7 +228,12 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
   // V rows of the whole key tile go to LDS once (B operand of dP = dO V^T
   // is read from there); K stays in registers as the B operand of S = Q K^T:
   // lane holds K[key][16*ks + 8*hh + 0..7].
-  load_tile<D, BK, NW>(s_v, (const uint16_t*)a.v + (int64_t)g * a.v_sh, a.v_st, it.row0, 0, it.nrows, wave, lane);
+  {
+    TileLoader<D, BK, NW> lvv;
+    const int64_t vst = a.v_st * 2;
+    lvv.init(vst, wave, lane);
+    lvv.issue(s_v, (const char*)a.v + ((int64_t)g * a.v_sh + (int64_t)it.row0 * a.v_st) * 2, it.nrows, vst);
+  }
   bf16x8 kreg[D / 16];
   {
     const uint16_t* ks_ = (const uint16_t*)a.k + (int64_t)(it.row0 + kr_) * a.k_st + (int64_t)g * a.k_sh + 8 * hh;
@@ -230,6 +245,10 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
     }
   }
 
+  const int64_t qst = a.q_st * 2, dst_ = a.do_st * 2;
+  TileLoader<D, BQ, NW> lq, ld;
+  lq.init(qst, wave, lane);
+  ld.init(dst_, wave, lane);
   const int nt0 = ceil_div(it.seg[0].n, BQ);
   const int nt1 = it.nseg > 1 ? ceil_div(it.seg[1].n, BQ) : 0;
   const int per_head = nt0 + nt1;
@@ -240,23 +259,24 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
     s = jt < nt0 ? 0 : 1;
     t0 = (jt - (s ? nt0 : 0)) * BQ;
   };
-  auto issue = [&](int j) {
+  auto issue = [&](int j, int buf) {
     int h, s, t0;
     tile_of(j, h, s, t0);
     const Segment& sg = it.seg[s];
-    const uint16_t* qb = (const uint16_t*)a.q + (int64_t)h * a.q_sh;
-    const uint16_t* db = (const uint16_t*)a.dout + (int64_t)h * a.do_sh;
-    load_tile<D, BQ, NW>(s_q[j & 1], qb, a.q_st, sg.row, t0, sg.n, wave, lane);
-    load_tile<D, BQ, NW>(s_do[j & 1], db, a.do_st, sg.row, t0, sg.n, wave, lane);
+    const int nvalid = min(BQ, sg.n - t0);
+    const int64_t row = sg.row + t0;
+    lq.issue(s_q[buf], (const char*)a.q + (row * a.q_st + (int64_t)h * a.q_sh) * 2, nvalid, qst);
+    ld.issue(s_do[buf], (const char*)a.dout + (row * a.do_st + (int64_t)h * a.do_sh) * 2, nvalid, dst_);
     if (wave < 2) {
-      const int r = min(t0 + lane, sg.n - 1);
-      const float* src = (wave == 0 ? a.lse : a.delta) + (int64_t)h * a.tq + sg.row + r;
-      float* dst = wave == 0 ? s_lse[j & 1] : s_dl[j & 1];
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+      // LSE (wave 0) or delta (wave 1) of the tile's rows; rows past the
+      // segment read as 0 and are masked
+      const float* src = (wave == 0 ? a.lse : a.delta) + (int64_t)h * a.tq + row;
+      float* dstl = wave == 0 ? s_lse[buf] : s_dl[buf];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(src, (unsigned)(nvalid * 4)),
+                                               (__attribute__((address_space(3))) void*)dstl, 4, lane * 4, 0, 0, 0);
     }
   };
-  issue(0);
+  issue(0, 0);
 
   f32x16 acc_k[D / 32], acc_v[D / 32];
 #pragma unroll
@@ -264,11 +284,11 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
 #pragma unroll
     for (int i = 0; i < 16; ++i) { acc_k[db][i] = 0.f; acc_v[db][i] = 0.f; }
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
+  auto tile = [&](int j, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     wait_loads();
     __syncthreads();
-    if (j + 1 < ntiles) issue(j + 1);
+    if (j + 1 < ntiles) issue(j + 1, buf ^ 1);
     int h, s, t0;
     tile_of(j, h, s, t0);
     (void)h;
@@ -319,6 +339,10 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
       acc_k[db] = mfma32(read_tr<D>(tq, 0, 32 * db, lane), ds0, acc_k[db]);
       acc_k[db] = mfma32(read_tr<D>(tq, 16, 32 * db, lane), ds1, acc_k[db]);
     }
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(j, std::integral_constant<int, 0>{});
+    if (j + 1 < ntiles) tile(j + 1, std::integral_constant<int, 1>{});
   }
 
   if (!key_ok) return;

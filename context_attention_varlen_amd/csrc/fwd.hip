@@ -28,6 +28,8 @@
 //
 // fp32 path: a plain per-row kernel (one query row per thread, exact expf)
 // for fp32 inputs; it exists for accuracy checks, not speed.
+#include <type_traits>
+
 #include "mfma.h"
 
 namespace cpattn {
@@ -57,25 +59,29 @@ void fwd_bf16_kernel(FwdArgs a) {
   if (item_rank >= a.hdr->n_items) return;
   const WorkItem it = a.items[a.order[item_rank]];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int col = lane & 31, hh = lane >> 5;
 
-  const uint16_t* qp = (const uint16_t*)a.q;
-  const uint16_t* kbase = (const uint16_t*)a.k + (int64_t)g * a.k_sh;
-  const uint16_t* vbase = (const uint16_t*)a.v + (int64_t)g * a.v_sh;
+  const int64_t kst = a.k_st * 2, vst = a.v_st * 2;     // row strides in bytes
+  const char* kbase = (const char*)a.k + (int64_t)g * a.k_sh * 2;
+  const char* vbase = (const char*)a.v + (int64_t)g * a.v_sh * 2;
+  TileLoader<D, BN, NW> lk, lv;
+  lk.init(kst, wave, lane);
+  lv.init(vst, wave, lane);
 
   const int nt0 = it.nseg > 0 ? ceil_div(it.seg[0].n, BN) : 0;
   const int nt1 = it.nseg > 1 ? ceil_div(it.seg[1].n, BN) : 0;
   const int ntiles = nt0 + nt1;
-  auto issue = [&](int j) {
+  auto issue = [&](int j, int buf) {
     const int s = j < nt0 ? 0 : 1;
     const int t0 = (j - (s ? nt0 : 0)) * BN;
     const Segment& sg = it.seg[s];
-    load_tile<D, BN, NW>(s_k[j & 1], kbase, a.k_st, sg.row, t0, sg.n, wave, lane);
-    load_tile<D, BN, NW>(s_v[j & 1], vbase, a.v_st, sg.row, t0, sg.n, wave, lane);
+    const int nvalid = min(BN, sg.n - t0);
+    const int64_t row = sg.row + t0;
+    lk.issue(s_k[buf], kbase + row * kst, nvalid, kst);
+    lv.issue(s_v[buf], vbase + row * vst, nvalid, vst);
   };
-  if (ntiles > 0) issue(0);
+  if (ntiles > 0) issue(0, 0);
 
   // Q operand (B of S^T = K Q^T): lane holds Q[row][16*ks + 8*hh + 0..7]
   bf16x8 qreg[QB][D / 16];
@@ -86,7 +92,7 @@ void fwd_bf16_kernel(FwdArgs a) {
     const int r = wave * QW + qb * 32 + col;
     row_ok[qb] = r < it.nrows;
     kr[qb] = key_ranges(a.mask, it.pos0 + r, a.tf_b, a.tf_n);
-    const uint16_t* src = qp + (int64_t)(it.row0 + r) * a.q_st + (int64_t)h * a.q_sh + 8 * hh;
+    const uint16_t* src = (const uint16_t*)a.q + (int64_t)(it.row0 + r) * a.q_st + (int64_t)h * a.q_sh + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
@@ -107,23 +113,22 @@ void fwd_bf16_kernel(FwdArgs a) {
       for (int i = 0; i < 16; ++i) acc_o[qb][db][i] = 0.f;
   }
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
+  // One key tile; BUF is a compile-time buffer index so every LDS offset is
+  // an immediate.
+  auto tile = [&](int j, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     wait_loads();
     __syncthreads();
-    if (j + 1 < ntiles) issue(j + 1);
+    if (j + 1 < ntiles) issue(j + 1, buf ^ 1);
     const int s = j < nt0 ? 0 : 1;
     const int t0 = (j - (s ? nt0 : 0)) * BN;
     const Segment sg = it.seg[s];
     const uint16_t* tk = s_k[buf];
     const uint16_t* tv = s_v[buf];
-
-    // Two 32-key sub-blocks per tile: S^T -> mask -> softmax -> PV each,
-    // which keeps only one 32 x 64 score block live per wave.
     const bool full = t0 >= sg.full_lo && t0 + BN <= sg.full_hi;
+    // two 32-key sub-blocks: S^T -> mask -> softmax -> PV
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
-      // ---- S^T = K Q^T ----
       f32x16 acc_s[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -135,12 +140,10 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc_s[qb] = mfma32(av, qreg[qb][ks], acc_s[qb]);
       }
-
-      // ---- mask (tiles not fully allowed) ----
       if (!full) {
-        const int kbase = t0 + kb * 32 + 4 * hh;      // key offset of register 0
-        const int rem = sg.n - kbase;                  // registers with offset >= rem are past the segment
-        const int pbase = sg.pos + kbase;
+        const int kbase0 = t0 + kb * 32 + 4 * hh;     // key offset of register 0
+        const int rem = sg.n - kbase0;                 // registers at offset >= rem are past the segment
+        const int pbase = sg.pos + kbase0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int off = 8 * (i >> 2) + (i & 3);
@@ -152,17 +155,14 @@ void fwd_bf16_kernel(FwdArgs a) {
           }
         }
       }
-
-      // ---- online softmax (row max in-lane + lane^32) ----
       float mt[QB];
       bool need = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float mx = acc_s[qb][0];
+        float mx = fmaxf(acc_s[qb][0], acc_s[qb][1]);
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, acc_s[qb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        mt[qb] = mx * a.scale_log2;
+        for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(acc_s[qb][i], acc_s[qb][i + 1]));
+        mt[qb] = max_halves(mx) * a.scale_log2;
         need |= mt[qb] > m_run[qb] + kRescale;
       }
       if (__any(need)) {
@@ -191,8 +191,6 @@ void fwd_bf16_kernel(FwdArgs a) {
         pb[qb][0] = pack_b(acc_s[qb], 0);
         pb[qb][1] = pack_b(acc_s[qb], 1);
       }
-
-      // ---- O^T += V^T P^T ----
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -202,12 +200,16 @@ void fwd_bf16_kernel(FwdArgs a) {
           for (int qb = 0; qb < QB; ++qb) acc_o[qb][db] = mfma32(av, pb[qb][hs], acc_o[qb][db]);
         }
     }
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(j, std::integral_constant<int, 0>{});
+    if (j + 1 < ntiles) tile(j + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue ----
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+    const float l = sum_halves(l_run[qb]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (!row_ok[qb]) continue;
     const int r = wave * QW + qb * 32 + col;

@@ -41,28 +41,64 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
   return row * D + ((chunk ^ swz<D>(row)) << 3);
 }
 
-// Direct global -> LDS copy of rows [t0, t0 + R) of a segment (rows past the
-// segment end repeat its last row: finite data that the mask discards) into
-// an R x D swizzled tile.  Every wave issues NINST/NW 1-KiB loads; lane p of
-// a load fetches the global chunk that belongs at LDS chunk p.
-template <int D, int R, int NW>
-__device__ __forceinline__ void load_tile(uint16_t* lds, const uint16_t* gbase, int64_t row_stride, int srow,
-                                          int t0, int n, int wave, int lane) {
-  constexpr int KCH = D / 8;
-  constexpr int NINST = R * KCH / 64;
-  static_assert(NINST % NW == 0, "tile loads split evenly over waves");
-#pragma unroll
-  for (int i = 0; i < NINST / NW; ++i) {
-    const int q = i * NW + wave;
-    const int p = q * 64 + lane;
-    const int row = p / KCH;
-    const int c = (p % KCH) ^ swz<D>(row);
-    const int r = min(t0 + row, n - 1);
-    const uint16_t* src = gbase + (int64_t)(srow + r) * row_stride + c * 8;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)(lds + q * 512), 16, 0, 0);
-  }
+// Buffer resource over `bytes` bytes from `base`: raw buffer loads at byte
+// offsets past the end return zeros without touching memory (the hardware
+// range check), which is how ragged tile tails are filled.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+
+// Direct global -> LDS loads of an R x D bf16 tile into a swizzled LDS tile.
+// Each wave issues PER loads of 1 KiB; lane p of load q fetches the global
+// 16-byte chunk that belongs at LDS chunk q*64 + p.  Lane byte offsets and
+// the wave-uniform LDS offsets are computed once; per tile only the scalar
+// buffer base and the number of valid rows change (rows past it read as 0).
+template <int D, int R, int NW>
+struct TileLoader {
+  static constexpr int KCH = D / 8;
+  static constexpr int NINST = R * KCH / 64;
+  static constexpr int PER = NINST / NW;
+  static_assert(NINST % NW == 0, "tile loads split evenly over waves");
+  int voff[PER];
+  int ldso[PER];
+
+  __device__ __forceinline__ void init(int64_t row_stride_bytes, int wave_u, int lane) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int q = i * NW + wave_u;
+      const int p = q * 64 + lane;
+      const int row = p / KCH;
+      const int c = (p % KCH) ^ swz<D>(row);
+      voff[i] = (int)(row * row_stride_bytes) + c * 16;
+      ldso[i] = q * 512;
+    }
+  }
+
+  // rows [0, nvalid) of the tile start at `tile_base` (bytes), consecutive
+  // rows `row_stride_bytes` apart
+  __device__ __forceinline__ void issue(uint16_t* lds, const void* tile_base, int nvalid,
+                                        int64_t row_stride_bytes) const {
+    const __amdgpu_buffer_rsrc_t rs = rows_rsrc(tile_base, (unsigned)(nvalid * row_stride_bytes));
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds + ldso[i]), 16,
+                                               voff[i], 0, 0, 0);
+  }
+};
+
+// Max of a value over the two 32-lane halves of the wave (the C-layout rows
+// of one accumulator column live in lanes l and l^32).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
