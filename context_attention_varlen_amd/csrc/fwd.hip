@@ -41,6 +41,8 @@ namespace cpattn {
 // tiles.  O / l and m + log2(l) use the same m, so the result is exact.
 constexpr float kRescale = 8.0f;
 
+
+
 // Waves per SIMD the kernel is compiled for: two when each wave owns 32
 // queries (so one wave's softmax overlaps the other's MFMAs), else one.
 template <int QB>
@@ -126,21 +128,48 @@ void fwd_bf16_kernel(FwdArgs a) {
     const uint16_t* tk = s_k[buf];
     const uint16_t* tv = s_v[buf];
     const bool full = t0 >= sg.full_lo && t0 + BN <= sg.full_hi;
-    // two 32-key sub-blocks: S^T -> mask -> softmax -> PV
+    // S^T for the whole 64-key tile (two independent MFMA chains per query
+    // block), then one softmax update, then PV.
+    f32x16 acc_s[QB][BN / 32];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-      f32x16 acc_s[QB];
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc_s[qb][i] = 0.f;
+        for (int i = 0; i < 16; ++i) acc_s[qb][kb][i] = 0.f;
+    // K operands are read four k-steps ahead of their MFMAs so the LDS
+    // latency hides behind the matrix pipe
+    constexpr int NKS = D / 16, NKB = BN / 32, PF = 4;
+    bf16x8 kop[PF][NKB];
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 av = read_row8<D>(tk, kb * 32 + col, 2 * ks + hh);
+    for (int ks = 0; ks < PF; ++ks)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc_s[qb] = mfma32(av, qreg[qb][ks], acc_s[qb]);
+      for (int kb = 0; kb < NKB; ++kb) kop[ks][kb] = read_row8<D>(tk, kb * 32 + col, 2 * ks + hh);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 cur[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) cur[kb] = kop[ks % PF][kb];
+      if (ks + PF < NKS) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) kop[ks % PF][kb] = read_row8<D>(tk, kb * 32 + col, 2 * (ks + PF) + hh);
       }
-      if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc_s[qb][kb] = mfma32(cur[kb], qreg[qb][ks], acc_s[qb][kb]);
+    }
+    // keep that order through the machine scheduler: PF*NKB reads first,
+    // then per k-step its MFMAs followed by the reads of k-step ks + PF
+    __builtin_amdgcn_sched_group_barrier(0x100, PF * NKB, 0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NKB * QB, 0);
+      if (ks + PF < NKS) __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
+    }
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb) {
         const int kbase0 = t0 + kb * 32 + 4 * hh;     // key offset of register 0
         const int rem = sg.n - kbase0;                 // registers at offset >= rem are past the segment
         const int pbase = sg.pos + kbase0;
@@ -151,55 +180,62 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             const bool ok = in & in_ranges(kr[qb], pbase + off);
-            acc_s[qb][i] = ok ? acc_s[qb][i] : -INFINITY;
+            acc_s[qb][kb][i] = ok ? acc_s[qb][kb][i] : -INFINITY;
           }
         }
       }
-      float mt[QB];
-      bool need = false;
+    }
+    float mt[QB];
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = acc_s[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int i = (kb == 0 ? 1 : 0); i + 1 < 16; i += 2) mx = max3f(mx, acc_s[qb][kb][i], acc_s[qb][kb][i + 1]);
+      mx = fmaxf(mx, acc_s[qb][BN / 32 - 1][15]);
+      mt[qb] = max_halves(mx) * a.scale_log2;
+      need |= mt[qb] > m_run[qb] + kRescale;
+    }
+    if (__any(need)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float mx = fmaxf(acc_s[qb][0], acc_s[qb][1]);
+        const float m_new = fmaxf(m_run[qb], mt[qb]);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
 #pragma unroll
-        for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(acc_s[qb][i], acc_s[qb][i + 1]));
-        mt[qb] = max_halves(mx) * a.scale_log2;
-        need |= mt[qb] > m_run[qb] + kRescale;
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc_o[qb][db][i] *= alpha;
       }
-      if (__any(need)) {
+    }
+    bf16x8 pb[QB][BN / 16];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float m_new = fmaxf(m_run[qb], mt[qb]);
-          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-          m_run[qb] = m_new;
-          l_run[qb] *= alpha;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc_o[qb][db][i] *= alpha;
-        }
-      }
-      bf16x8 pb[QB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+      for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(acc_s[qb][i] * a.scale_log2 - m_use);
-          acc_s[qb][i] = p;
+          const float p = __builtin_amdgcn_exp2f(acc_s[qb][kb][i] * a.scale_log2 - m_use);
+          acc_s[qb][kb][i] = p;
           l_run[qb] += p;
         }
-        pb[qb][0] = pack_b(acc_s[qb], 0);
-        pb[qb][1] = pack_b(acc_s[qb], 1);
+        pb[qb][2 * kb] = pack_b(acc_s[qb][kb], 0);
+        pb[qb][2 * kb + 1] = pack_b(acc_s[qb][kb], 1);
       }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const bf16x8 av = read_tr<D>(tv, 32 * kb + 16 * hs, 32 * db, lane);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc_o[qb][db] = mfma32(av, pb[qb][hs], acc_o[qb][db]);
-        }
     }
+    // consecutive MFMAs go to different accumulators (independent chains)
+#pragma unroll
+    for (int ps = 0; ps < BN / 16; ++ps)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 av = read_tr<D>(tv, 16 * ps, 32 * db, lane);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc_o[qb][db] = mfma32(av, pb[qb][ps], acc_o[qb][db]);
+      }
   };
   for (int j = 0; j < ntiles; j += 2) {
     tile(j, std::integral_constant<int, 0>{});
@@ -278,6 +314,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
 #ifndef CPATTN_FWD_QB
 #define CPATTN_FWD_QB 1
 #endif
+
 #ifndef CPATTN_FWD_WAVES
 #define CPATTN_FWD_WAVES 4
 #endif

@@ -98,6 +98,13 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
 
+// Three-input max (v_max3_f32); the compiler forms few of these on its own.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
