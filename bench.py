@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--workload", default="long_tail")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a device copy of a known size (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -264,6 +266,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        # 1 GiB read + 1 GiB written per copy: the reference that scales the
+        # FETCH_SIZE / WRITE_SIZE counters of the attention kernels
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 4 * n, "bytes_written_per_copy": 4 * n,
+                                               "copies": 4}}), flush=True)
+        return
     import context_attention_varlen_amd as c
     import workloads
 
