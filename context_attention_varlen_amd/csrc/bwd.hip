@@ -38,6 +38,14 @@ constexpr int kDqWaves = 4, kDqQB = 1;            // dq: 4 waves x 32 queries
 constexpr int kDkvWaves = 4;                       // dkv: 4 waves x 32 keys
 constexpr int kBwdBQ = 32;                         // query rows per LDS tile (dkv)
 constexpr int kBwdBK = 64;                         // key rows per LDS tile (dq)
+#ifndef CPATTN_DKV_PF
+#define CPATTN_DKV_PF 2
+#endif
+#ifndef CPATTN_DKV_TPF
+#define CPATTN_DKV_TPF 2
+#endif
+constexpr int kDkvPF = CPATTN_DKV_PF;               // dkv: S/dP operand reads ahead (k-steps)
+constexpr int kDkvTPF = CPATTN_DKV_TPF;             // dkv: dV/dK transposed reads ahead (products)
 
 // ---------------------------------------------------------------------------
 // dq kernel (bf16)
@@ -133,8 +141,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, uint16_t*
         for (int i = 0; i < 16; ++i) { st[qb][i] = 0.f; dpt[qb][i] = 0.f; }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 ak = read_row8<D>(tk, kb * 32 + col, 2 * ks + hh);
-        const bf16x8 av = read_row8<D>(tv, kb * 32 + col, 2 * ks + hh);
+        const bf16x8 ak = read_row8<D>(tk, kb * 32, col, ks, hh);
+        const bf16x8 av = read_row8<D>(tv, kb * 32, col, ks, hh);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           st[qb] = mfma32(ak, qreg[qb][ks], st[qb]);
@@ -251,32 +259,39 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
   ld.init(dst_, wave, lane);
   const int nt0 = ceil_div(it.seg[0].n, BQ);
   const int nt1 = it.nseg > 1 ? ceil_div(it.seg[1].n, BQ) : 0;
-  const int per_head = nt0 + nt1;
-  const int ntiles = per_head * a.grp;
-  auto tile_of = [&](int j, int& h, int& s, int& t0) {
-    const int jh = j / per_head, jt = j - jh * per_head;
-    h = g * a.grp + jh;
-    s = jt < nt0 ? 0 : 1;
-    t0 = (jt - (s ? nt0 : 0)) * BQ;
+  const int ntiles = (nt0 + nt1) * a.grp;
+  // Tiles run q-head by q-head, and within a head over segment 0 then 1;
+  // the position advances without division. Segment fields are picked by
+  // select so they stay in scalar registers.
+  struct TilePos { int h, s, t0; };
+  auto seg_n = [&](int sgi) { return sgi ? it.seg[1].n : it.seg[0].n; };
+  auto next_pos = [&](TilePos tp) {
+    tp.t0 += BQ;
+    if (tp.t0 >= seg_n(tp.s)) {
+      tp.t0 = 0;
+      const bool to1 = tp.s == 0 && it.nseg > 1;
+      tp.h += to1 ? 0 : 1;
+      tp.s = to1 ? 1 : 0;
+    }
+    return tp;
   };
-  auto issue = [&](int j, int buf) {
-    int h, s, t0;
-    tile_of(j, h, s, t0);
-    const Segment& sg = it.seg[s];
-    const int nvalid = min(BQ, sg.n - t0);
-    const int64_t row = sg.row + t0;
-    lq.issue(s_q[buf], (const char*)a.q + (row * a.q_st + (int64_t)h * a.q_sh) * 2, nvalid, qst);
-    ld.issue(s_do[buf], (const char*)a.dout + (row * a.do_st + (int64_t)h * a.do_sh) * 2, nvalid, dst_);
+  auto issue = [&](const TilePos& tp, int buf) {
+    const int nvalid = min(BQ, seg_n(tp.s) - tp.t0);
+    const int64_t row = (tp.s ? it.seg[1].row : it.seg[0].row) + tp.t0;
+    lq.issue(s_q[buf], (const char*)a.q + (row * a.q_st + (int64_t)tp.h * a.q_sh) * 2, nvalid, qst);
+    ld.issue(s_do[buf], (const char*)a.dout + (row * a.do_st + (int64_t)tp.h * a.do_sh) * 2, nvalid, dst_);
     if (wave < 2) {
       // LSE (wave 0) or delta (wave 1) of the tile's rows; rows past the
       // segment read as 0 and are masked
-      const float* src = (wave == 0 ? a.lse : a.delta) + (int64_t)h * a.tq + row;
+      const float* src = (wave == 0 ? a.lse : a.delta) + (int64_t)tp.h * a.tq + row;
       float* dstl = wave == 0 ? s_lse[buf] : s_dl[buf];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rows_rsrc(src, (unsigned)(nvalid * 4)),
                                                (__attribute__((address_space(3))) void*)dstl, 4, lane * 4, 0, 0, 0);
     }
   };
-  issue(0, 0);
+  TilePos cur = {g * a.grp, 0, 0};  // tile being computed
+  TilePos nxt = next_pos(cur);      // tile loaded next
+  issue(cur, 0);
 
   f32x16 acc_k[D / 32], acc_v[D / 32];
 #pragma unroll
@@ -284,60 +299,120 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
 #pragma unroll
     for (int i = 0; i < 16; ++i) { acc_k[db][i] = 0.f; acc_v[db][i] = 0.f; }
 
+  constexpr int NK = D / 16;     // k-steps of S and dP
+  constexpr int NT = D / 8;      // dV and dK products
+  constexpr int PF = kDkvPF, TPF = kDkvTPF;
   auto tile = [&](int j, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     wait_loads();
     __syncthreads();
-    if (j + 1 < ntiles) issue(j + 1, buf ^ 1);
-    int h, s, t0;
-    tile_of(j, h, s, t0);
-    (void)h;
-    const Segment sg = it.seg[s];
+    if (j + 1 < ntiles) issue(nxt, buf ^ 1);
+    const int t0 = cur.t0;
+    const int sn = seg_n(cur.s);
+    const int spos = cur.s ? it.seg[1].pos : it.seg[0].pos;
+    const bool full = t0 >= (cur.s ? it.seg[1].full_lo : it.seg[0].full_lo) &&
+                      t0 + BQ <= (cur.s ? it.seg[1].full_hi : it.seg[0].full_hi);
+    cur = nxt;
+    nxt = next_pos(nxt);
     const uint16_t* tq = s_q[buf];
     const uint16_t* tdo = s_do[buf];
-    const bool full = t0 >= sg.full_lo && t0 + BQ <= sg.full_hi;
 
-    // S = Q K^T and dP = dO V^T for the tile's 32 query rows x this wave's 32 keys
+    // The tile is software-pipelined by hand: operand reads are issued PF
+    // (S, dP) or TPF (dV, dK) products ahead, and each step is fenced so
+    // the order stays as written. Per wave: S = Q K^T (one accumulator
+    // chain), then dP = dO V^T with P = exp(S*scale - lse) computed under
+    // it, then dV^T += dO^T P^T with dS = P * (dP - delta) computed under
+    // it, then dK^T += Q^T dS^T. Accumulator element i of a lane holds
+    // query row 8*(i/4) + 4*hh + i%4 and key column `col`.
     f32x16 st, dp;
 #pragma unroll
     for (int i = 0; i < 16; ++i) { st[i] = 0.f; dp[i] = 0.f; }
+    bf16x8 qa[NK], da[NK], va[NK];
+    auto read_sdp = [&](int u) {  // operands of product u of the S, dP sequence
+      if (u < NK) {
+        qa[u] = read_row8<D>(tq, 0, col, u, hh);
+      } else {
+        da[u - NK] = read_row8<D>(tdo, 0, col, u - NK, hh);
+        va[u - NK] = read_row8<D>(s_v, wave * 32, col, u - NK, hh);
+      }
+    };
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 aq = read_row8<D>(tq, col, 2 * ks + hh);
-      const bf16x8 ad = read_row8<D>(tdo, col, 2 * ks + hh);
-      const bf16x8 bv = read_row8<D>(s_v, kr_, 2 * ks + hh);
-      st = mfma32(aq, kreg[ks], st);
-      dp = mfma32(ad, bv, dp);
+    for (int u = 0; u < PF; ++u) read_sdp(u);
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      if (ks + PF < 2 * NK) read_sdp(ks + PF);
+      st = mfma32(qa[ks], kreg[ks], st);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // rows of this lane: q = 8*(i/4) + 4*hh + i%4
-    const int qofs0 = t0 + 4 * hh;
-    const int rem = sg.n - qofs0;
-    const int pbase = sg.pos + qofs0;
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 l4 = *(const f32x4*)(&s_lse[buf][4 * hh + 8 * i4]);
-      const f32x4 d4 = *(const f32x4*)(&s_dl[buf][4 * hh + 8 * i4]);
+    // exp of the 4 rows of group g4 (lse read two products earlier); a row
+    // with lse = -inf has no allowed key: it only occurs in partial tiles,
+    // where the mask below zeroes it
+    f32x4 l4[4];
+    auto exp_group = [&](int g4) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 4 * i4 + e;
-        const int off = 8 * i4 + e;
-        const float l = l4[e];
-        const float lse2 = l == -INFINITY ? INFINITY : l * 1.4426950408889634f;
-        float p = __builtin_amdgcn_exp2f(st[i] * a.scale_log2 - lse2);
-        const bool ok = full | ((off < rem) & in_ranges(qrng, pbase + off));
-        p = ok ? p : 0.f;
-        st[i] = p;
-        dp[i] = p * (dp[i] - d4[e]);
+        float pv = __builtin_amdgcn_exp2f(st[4 * g4 + e] * a.scale_log2 - l4[g4][e] * 1.4426950408889634f);
+        asm("" : "+v"(pv));  // opaque to folds: the exp stays ahead of the mask branch
+        st[4 * g4 + e] = pv;
+      }
+    };
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      if (NK + ks + PF < 2 * NK) read_sdp(NK + ks + PF);
+      if (ks < 4) l4[ks] = *(const f32x4*)(&s_lse[buf][4 * hh + 8 * ks]);
+      dp = mfma32(da[ks], va[ks], dp);
+      if (ks >= 2 && ks < 6) exp_group(ks - 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int g4 = NK - 2; g4 < 4; ++g4) exp_group(g4);  // groups past the last product (D = 64)
+
+    bf16x8 ta[NT];
+    auto read_t = [&](int m) {  // operand of product m: dV (m < NT/2) or dK
+      const int hf = (m % (NT / 2)) / (D / 32), db = m % (D / 32);
+      ta[m] = read_tr<D>(m < NT / 2 ? tdo : tq, 16 * hf, 32 * db, lane);
+    };
+#pragma unroll
+    for (int m = 0; m < TPF; ++m) read_t(m);
+    if (!full) {
+      const int qofs0 = t0 + 4 * hh;
+      const int rem = sn - qofs0;
+      const int pbase = spos + qofs0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int off = 8 * (i >> 2) + (i & 3);
+        st[i] = ((off < rem) & in_ranges(qrng, pbase + off)) ? st[i] : 0.f;
       }
     }
-    const bf16x8 pb0 = pack_b(st, 0), pb1 = pack_b(st, 1);
-    const bf16x8 ds0 = pack_b(dp, 0), ds1 = pack_b(dp, 1);
+    const bf16x8 pb[2] = {pack_b(st, 0), pack_b(st, 1)};
+    bf16x8 ds[2];
+    f32x4 d4[4];
+    auto ds_group = [&](int g4) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      acc_v[db] = mfma32(read_tr<D>(tdo, 0, 32 * db, lane), pb0, acc_v[db]);
-      acc_v[db] = mfma32(read_tr<D>(tdo, 16, 32 * db, lane), pb1, acc_v[db]);
-      acc_k[db] = mfma32(read_tr<D>(tq, 0, 32 * db, lane), ds0, acc_k[db]);
-      acc_k[db] = mfma32(read_tr<D>(tq, 16, 32 * db, lane), ds1, acc_k[db]);
+      for (int e = 0; e < 4; ++e) dp[4 * g4 + e] = st[4 * g4 + e] * (dp[4 * g4 + e] - d4[g4][e]);
+    };
+#pragma unroll
+    for (int m = 0; m < NT / 2; ++m) {
+      if (m + TPF < NT) read_t(m + TPF);
+      if (m < 4) d4[m] = *(const f32x4*)(&s_dl[buf][4 * hh + 8 * m]);
+      const int hf = m / (D / 32), db = m % (D / 32);
+      acc_v[db] = mfma32(ta[m], pb[hf], acc_v[db]);
+      if (m >= 1 && m <= 4) ds_group(m - 1);
+      if (m == 3) ds[0] = pack_b(dp, 0);
+      if (m == 5) ds[1] = pack_b(dp, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // groups and packs past the last dV product (D = 64)
+#pragma unroll
+    for (int g4 = NT / 2 - 1; g4 < 4; ++g4) ds_group(g4);
+    if (3 >= NT / 2) ds[0] = pack_b(dp, 0);
+    if (5 >= NT / 2) ds[1] = pack_b(dp, 1);
+#pragma unroll
+    for (int m = NT / 2; m < NT; ++m) {
+      if (m + TPF < NT) read_t(m + TPF);
+      const int hf = (m - NT / 2) / (D / 32), db = m % (D / 32);
+      acc_k[db] = mfma32(ta[m], ds[hf], acc_k[db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   for (int j = 0; j < ntiles; j += 2) {

@@ -144,7 +144,7 @@ void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < PF; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) kop[ks][kb] = read_row8<D>(tk, kb * 32 + col, 2 * ks + hh);
+      for (int kb = 0; kb < NKB; ++kb) kop[ks][kb] = read_row8<D>(tk, kb * 32, col, ks, hh);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       bf16x8 cur[NKB];
@@ -152,7 +152,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       for (int kb = 0; kb < NKB; ++kb) cur[kb] = kop[ks % PF][kb];
       if (ks + PF < NKS) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) kop[ks % PF][kb] = read_row8<D>(tk, kb * 32 + col, 2 * (ks + PF) + hh);
+        for (int kb = 0; kb < NKB; ++kb) kop[ks % PF][kb] = read_row8<D>(tk, kb * 32, col, ks + PF, hh);
       }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)

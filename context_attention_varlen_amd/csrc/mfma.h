@@ -24,21 +24,37 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Row-major bf16 tile of D columns in LDS, 16-byte chunks XOR-swizzled by
-//   f(row) = ((row & 3) << (log2(D/8) - 2)) | ((row >> 2) & (D/32 - 1)).
-// 16 (D=128) or 8 (D=64) consecutive rows read at one logical chunk land in
-// distinct chunks (row-wise 128-bit reads), and 4 consecutive rows x 4
-// (or 2) adjacent chunks land in distinct chunks (transposed reads).
+// bf16 tile of D columns in LDS, stored in 1 KiB blocks of RG = 512/D rows.
+// Inside a block, 64-byte pieces (4 chunks of 16 bytes) of the RG rows are
+// interleaved: piece cg = chunk/4 of row r sits at cg*RG*64 + (r%RG)*64
+// bytes, and its 4 chunks are XOR-permuted by s(r) = (r/4) % 4:
+//   offset(r, c) = (r/RG)*1024 + (c/4)*RG*64 + (r%RG)*64 + ((c%4) ^ s(r))*16.
+// Modulo 256 bytes this is (r%4)*64 + ((c%4) ^ s(r))*16, so 16 consecutive
+// rows read at one chunk (row-wise 128-bit reads) and 4 consecutive rows x 4
+// adjacent chunks (transposed reads) both touch 16 distinct 16-byte bank
+// slots. The chunk index enters only through c/4 (a constant for a given
+// k-step) and c%4, so a lane needs two base addresses per tile and every
+// k-step is an immediate offset from one of them. One direct-load
+// instruction (64 lanes x 16 bytes) fills exactly one block.
+//
+// Element offset of chunk 4*cg + cl of row rc + rl, split so that the
+// compiler sees which parts are constant: rc (constant or wave-uniform) is
+// a multiple of 16, or a multiple of 8 with rl < 8; rl >= 0 is the
+// lane-dependent row part, cg the constant chunk group and 0 <= cl < 4 the
+// lane-dependent chunk part. Under those conditions (rc + rl)/4 % 4 equals
+// (rc/4 % 4) ^ (rl/4 % 4).
 template <int D>
-__device__ __forceinline__ int swz(int row) {
-  constexpr int KCH = D / 8;
-  constexpr int SH = KCH == 16 ? 2 : 1;
-  return ((row & 3) << SH) | ((row >> 2) & (KCH / 4 - 1));
+__device__ __forceinline__ int tile_off_split(int rc, int rl, int cg, int cl) {
+  constexpr int LRG = D == 128 ? 2 : 3;  // log2 of RG = 512 / D
+  const unsigned urc = (unsigned)rc, url = (unsigned)rl, ucl = (unsigned)cl;
+  const unsigned s = ((urc >> 2) & 3u) ^ ((url >> 2) & 3u);
+  return (int)(((urc >> LRG) << 9) + ((url >> LRG) << 9) + ((url & ((1u << LRG) - 1)) << 5) +
+               (unsigned)cg * (32u << LRG) + ((ucl ^ s) << 3));
 }
 
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int chunk) {
-  return row * D + ((chunk ^ swz<D>(row)) << 3);
+  return tile_off_split<D>(0, row, chunk >> 2, chunk & 3);
 }
 
 // Buffer resource over `bytes` bytes from `base`: raw buffer loads at byte
@@ -48,7 +64,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, un
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Direct global -> LDS loads of an R x D bf16 tile into a swizzled LDS tile.
+// Direct global -> LDS loads of an R x D bf16 tile into the LDS tile layout.
 // Each wave issues PER loads of 1 KiB; lane p of load q fetches the global
 // 16-byte chunk that belongs at LDS chunk q*64 + p.  Lane byte offsets and
 // the wave-uniform LDS offsets are computed once; per tile only the scalar
@@ -59,16 +75,18 @@ struct TileLoader {
   static constexpr int NINST = R * KCH / 64;
   static constexpr int PER = NINST / NW;
   static_assert(NINST % NW == 0, "tile loads split evenly over waves");
+  static_assert(R % (512 / D) == 0, "whole 1 KiB blocks");
   int voff[PER];
   int ldso[PER];
 
   __device__ __forceinline__ void init(int64_t row_stride_bytes, int wave_u, int lane) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
+      // load q fills LDS block q: lane p lands at 16*p bytes into it
+      constexpr int RG = 512 / D;
       const int q = i * NW + wave_u;
-      const int p = q * 64 + lane;
-      const int row = p / KCH;
-      const int c = (p % KCH) ^ swz<D>(row);
+      const int row = q * RG + (lane >> 2) % RG;
+      const int c = ((lane >> 2) / RG) * 4 + ((lane & 3) ^ ((row >> 2) & 3));
       voff[i] = (int)(row * row_stride_bytes) + c * 16;
       ldso[i] = q * 512;
     }
@@ -109,10 +127,18 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// 16-byte row read: A (or B) operand slot for row `row`, logical chunk `chunk`.
+// 16-byte row read: the A (or B) operand slot of k-step ks for tile row
+// rc + rl (rc a multiple of 16), i.e. chunk 2*ks + hh of that row.
+typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+
+// LDS pointer of a tile: offsets added to it stay 32-bit, so constant parts
+// fold into the instructions' immediate offsets
+__device__ __forceinline__ lds_u16* lds_ptr(const uint16_t* tile) { return (lds_u16*)tile; }
+
 template <int D>
-__device__ __forceinline__ bf16x8 read_row8(const uint16_t* tile, int row, int chunk) {
-  return __builtin_bit_cast(bf16x8, *(const u32x4*)(tile + tile_off<D>(row, chunk)));
+__device__ __forceinline__ bf16x8 read_row8(const uint16_t* tile, int rc, int rl, int ks, int hh) {
+  lds_u16* p = lds_ptr(tile) + tile_off_split<D>(rc, rl, ks >> 1, 2 * (ks & 1) + hh);
+  return __builtin_bit_cast(bf16x8, *(__attribute__((address_space(3))) const u32x4*)p);
 }
 
 // Transposed operand: the 32 x 16 operand whose MFMA row index runs along
@@ -124,14 +150,14 @@ __device__ __forceinline__ bf16x8 read_row8(const uint16_t* tile, int row, int c
 // into two 16-row k-steps.
 template <int D>
 __device__ __forceinline__ bf16x8 read_tr(const uint16_t* tile, int r0, int c0, int lane) {
+  // r0 is a multiple of 16 and c0 of 32: row r0 + (8t + 4hh + j/4), column
+  // c0 + 16mh + 4(j%4) is chunk 4*(c0/32) + (2mh + (j%4)/2), element 4(j%2)
   const int j = lane & 15, mh = (lane >> 4) & 1, hh = lane >> 5;
-  const int col = c0 + 16 * mh + 4 * (j & 3);
   s16x4 v[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int row = r0 + 8 * t + 4 * hh + (j >> 2);
-    const int off = row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
-    v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(tile + off));
+    const int off = tile_off_split<D>(r0 + 8 * t, 4 * hh + (j >> 2), c0 >> 5, 2 * mh + ((j & 3) >> 1)) + 4 * (j & 1);
+    v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(lds_ptr(tile) + off));
   }
   u32x4 r;
   r[0] = __builtin_bit_cast(u32x2, v[0])[0];
