@@ -44,6 +44,10 @@ constexpr int kBwdBK = 64;                         // key rows per LDS tile (dq)
 #ifndef CPATTN_DKV_TPF
 #define CPATTN_DKV_TPF 2
 #endif
+#ifndef CPATTN_DQ_PF
+#define CPATTN_DQ_PF 2
+#endif
+constexpr int kDqPF = CPATTN_DQ_PF;                 // dq: operand reads ahead (products)
 constexpr int kDkvPF = CPATTN_DKV_PF;               // dkv: S/dP operand reads ahead (k-steps)
 constexpr int kDkvTPF = CPATTN_DKV_TPF;             // dkv: dV/dK transposed reads ahead (products)
 
@@ -121,6 +125,9 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, uint16_t*
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[qb][db][i] = 0.f;
 
+  static_assert(QB == 1 && BN == 64, "the dQ tile schedule covers one 32-query block and two 32-key blocks");
+  constexpr int NK = D / 16;   // k-steps of S^T and dP^T; also dQ products per key block
+  constexpr int PF = kDqPF;
   auto tile = [&](int j, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     wait_loads();
@@ -132,57 +139,128 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, uint16_t*
     const uint16_t* tk = s_k[buf];
     const uint16_t* tv = s_v[buf];
     const bool full = t0 >= sg.full_lo && t0 + BN <= sg.full_hi;
+
+    // Hand-pipelined tile of 64 keys (key blocks 0, 1) x this wave's 32
+    // queries. Products in order: S0^T, dP0^T, S1^T, dP1^T (NK each, one
+    // accumulator chain each; S^T = K Q^T, dP^T = V dO^T), then dQ0^T and
+    // dQ1^T (dQ^T += K^T dS^T). VALU work rides under the products:
+    // exp(S0) under dP0, dS0 under S1, exp(S1) under dP1, dS1 under dQ0.
+    // Operands are read PF products ahead; every step is fenced. Element i
+    // of a lane holds key 8*(i/4) + 4*hh + i%4 of its block, query `col`.
+    f32x16 st[2], dpt[2];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-      f32x16 st[QB], dpt[QB];
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { st[qb][i] = 0.f; dpt[qb][i] = 0.f; }
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 ak = read_row8<D>(tk, kb * 32, col, ks, hh);
-        const bf16x8 av = read_row8<D>(tv, kb * 32, col, ks, hh);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          st[qb] = mfma32(ak, qreg[qb][ks], st[qb]);
-          dpt[qb] = mfma32(av, doreg[qb][ks], dpt[qb]);
-        }
+      for (int i = 0; i < 16; ++i) { st[b][i] = 0.f; dpt[b][i] = 0.f; }
+    bf16x8 op[6 * NK];
+    auto read_op = [&](int u) {
+      if (u < 4 * NK) {  // row operand: block u / NK is S0, dP0, S1, dP1
+        const int blk = u / NK, ks = u % NK;
+        op[u] = read_row8<D>((blk & 1) ? tv : tk, 32 * (blk >> 1), col, ks, hh);
+      } else {           // transposed K operand of dQ product m of key block kb
+        const int kb = (u - 4 * NK) / NK, m = (u - 4 * NK) % NK;
+        op[u] = read_tr<D>(tk, 32 * kb + 16 * (m & 1), 32 * (m >> 1), lane);
       }
+    };
+    auto exp_group = [&](int b, int g4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float pv = __builtin_amdgcn_exp2f(st[b][4 * g4 + e] * a.scale_log2 - lse2[0]);
+        asm("" : "+v"(pv));  // opaque to folds: the exp stays ahead of the mask branch
+        st[b][4 * g4 + e] = pv;
+      }
+    };
+    auto mask_block = [&](int b) {
       if (!full) {
-        const int kb0 = t0 + kb * 32 + 4 * hh;
+        const int kb0 = t0 + b * 32 + 4 * hh;
         const int rem = sg.n - kb0;
         const int pbase = sg.pos + kb0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int off = 8 * (i >> 2) + (i & 3);
-          const bool in = off < rem;
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const bool ok = in & in_ranges(kr[qb], pbase + off);
-            st[qb][i] = ok ? st[qb][i] : -INFINITY;
-          }
+          st[b][i] = ((off < rem) & in_ranges(kr[0], pbase + off)) ? st[b][i] : 0.f;
         }
       }
-      bf16x8 dsb[QB][2];
+    };
+    bf16x8 dsb[2][2];
+    auto ds_group = [&](int b, int g4) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
+      for (int e = 0; e < 4; ++e) st[b][4 * g4 + e] = st[b][4 * g4 + e] * (dpt[b][4 * g4 + e] - dlt[0]);
+    };
+    // VALU riding under product ks of a phase: four groups from step 1 (dS)
+    // or 2 (exp) on, the packs after them; what does not fit (D = 64) follows
+    // the phase
+    auto under_exp = [&](int b, int ks) { if (ks >= 2 && ks < 6) exp_group(b, ks - 2); };
+    auto tail_exp = [&](int b) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(st[qb][i] * a.scale_log2 - lse2[qb]);
-          st[qb][i] = p * (dpt[qb][i] - dlt[qb]);
-        }
-        dsb[qb][0] = pack_b(st[qb], 0);
-        dsb[qb][1] = pack_b(st[qb], 1);
-      }
+      for (int g4 = NK - 2; g4 < 4; ++g4) exp_group(b, g4);
+    };
+    // the packed dS is pinned where it is formed: it is used only after the
+    // next mask branch, and would otherwise be sunk past it
+    auto pack_ds = [&](int b, int hf) {
+      dsb[b][hf] = pack_b(st[b], hf);
+      asm volatile("" : "+v"(dsb[b][hf]));
+    };
+    auto under_ds = [&](int b, int ks) {
+      if (ks >= 1 && ks < 5) ds_group(b, ks - 1);
+      if (ks == 3) pack_ds(b, 0);
+      if (ks == 5) pack_ds(b, 1);
+    };
+    auto tail_ds = [&](int b) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int g4 = NK - 1; g4 < 4; ++g4) ds_group(b, g4);
+      if (3 >= NK) pack_ds(b, 0);
+      if (5 >= NK) pack_ds(b, 1);
+    };
+
 #pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          const bf16x8 akt = read_tr<D>(tk, 32 * kb + 16 * hs, 32 * db, lane);
+    for (int u = 0; u < PF; ++u) read_op(u);
+    auto step = [&](int u) { if (u + PF < 6 * NK) read_op(u + PF); };
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(akt, dsb[qb][hs], acc[qb][db]);
-        }
+    for (int ks = 0; ks < NK; ++ks) {           // S0^T
+      step(ks);
+      st[0] = mfma32(op[ks], qreg[0][ks], st[0]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {           // dP0^T, exp(S0)
+      step(NK + ks);
+      dpt[0] = mfma32(op[NK + ks], doreg[0][ks], dpt[0]);
+      under_exp(0, ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    tail_exp(0);
+    mask_block(0);
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {           // S1^T, dS0
+      step(2 * NK + ks);
+      st[1] = mfma32(op[2 * NK + ks], qreg[0][ks], st[1]);
+      under_ds(0, ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    tail_ds(0);
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {           // dP1^T, exp(S1)
+      step(3 * NK + ks);
+      dpt[1] = mfma32(op[3 * NK + ks], doreg[0][ks], dpt[1]);
+      under_exp(1, ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    tail_exp(1);
+    mask_block(1);
+#pragma unroll
+    for (int m = 0; m < NK; ++m) {              // dQ0^T, dS1
+      step(4 * NK + m);
+      acc[0][m >> 1] = mfma32(op[4 * NK + m], dsb[0][m & 1], acc[0][m >> 1]);
+      under_ds(1, m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    tail_ds(1);
+#pragma unroll
+    for (int m = 0; m < NK; ++m) {              // dQ1^T
+      step(5 * NK + m);
+      acc[0][m >> 1] = mfma32(op[5 * NK + m], dsb[1][m & 1], acc[0][m >> 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   for (int j = 0; j < ntiles; j += 2) {
