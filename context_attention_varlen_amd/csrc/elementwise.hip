@@ -7,21 +7,6 @@ namespace cpattn {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void unpack8(const void* p, bool bf16, float* out) {
-  if (bf16) {
-    const u32x4 raw = *(const u32x4*)p;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __uint_as_float(raw[i] << 16);
-      out[2 * i + 1] = __uint_as_float(raw[i] & 0xffff0000u);
-    }
-  } else {
-    const f32x4 a = ((const f32x4*)p)[0], b = ((const f32x4*)p)[1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { out[i] = a[i]; out[4 + i] = b[i]; }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // LSE merge.  Ring Attention ("Scaling Video Training with Parallelism",
 // section 2) produces one partial (out, lse) per key/value block; two partial
@@ -35,52 +20,68 @@ __device__ __forceinline__ void unpack8(const void* p, bool bf16, float* out) {
 // ---------------------------------------------------------------------------
 
 
+// Streaming loads and stores bypass cache residency (nontemporal): every
+// byte is touched once.
+template <class T>
+__device__ __forceinline__ T ld_nt(const T* p) { return __builtin_nontemporal_load(p); }
+template <class T>
+__device__ __forceinline__ void st_nt(T v, T* p) { __builtin_nontemporal_store(v, p); }
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// 4 elements of a row at element offset e: fp32, or bf16 widened to fp32
+template <bool BF16>
+__device__ __forceinline__ f32x4 load4(const void* row, int e) {
+  if (BF16) {
+    const u32x2 raw = ld_nt((const u32x2*)((const uint16_t*)row + e));
+    return f32x4{__uint_as_float(raw[0] << 16), __uint_as_float(raw[0] & 0xffff0000u),
+                 __uint_as_float(raw[1] << 16), __uint_as_float(raw[1] & 0xffff0000u)};
+  }
+  return ld_nt((const f32x4*)((const float*)row + e));
+}
+
+// Rows are visited token-major (r = t*H + h), the order of `out` and of the
+// partial in memory, so both stream contiguously; thread c of a row owns
+// elements [4c, 4c + 4). The head-major LSE reads of 16 consecutive tokens
+// share one cache line.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  constexpr int TPR = D / 8;  // threads per row
+  constexpr int TPR = D / 4;  // threads per row
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t r = gid / TPR;
   const int c = (int)(gid - r * TPR);
   if (r >= (int64_t)a.heads * a.tokens) return;
-  const int h = (int)(r / a.tokens);
-  const int64_t t = r - (int64_t)h * a.tokens;
-  const float lp = a.lsep[r];
+  const int64_t t = r / a.heads;
+  const int h = (int)(r - t * a.heads);
+  const int64_t li = (int64_t)h * a.tokens + t;
+  const float lp = a.lsep[li];
   if (lp == -INFINITY) return;
-  const float lo = a.lse[r];
-  float* orow = a.out + (t * a.heads + h) * D + c * 8;
-  const char* prow = (const char*)a.op + ((t * a.op_st + (int64_t)h * a.op_sh) + c * 8) * (BF16 ? 2 : 4);
-  float p[8];
-  unpack8(prow, BF16, p);
-  float w_o, w_p, nl;
+  const float lo = a.lse[li];
+  float* o = a.out + r * D + 4 * c;
+  const void* prow = (const char*)a.op + (t * a.op_st + (int64_t)h * a.op_sh) * (BF16 ? 2 : 4);
+  const f32x4 p = load4<BF16>(prow, 4 * c);
+  f32x4 v;
+  float nl;
   if (lo == -INFINITY) {
-    w_o = 0.f; w_p = 1.f; nl = lp;
+    v = p;
+    nl = lp;
   } else {
     const float m = fmaxf(lo, lp);
     const float eo = __expf(lo - m), ep = __expf(lp - m);
     const float s = eo + ep;
     nl = m + __logf(s);
     const float inv = 1.f / s;
-    w_o = eo * inv;
-    w_p = ep * inv;
-  }
-  f32x4 o0 = ((f32x4*)orow)[0], o1 = ((f32x4*)orow)[1];
-  if (lo == -INFINITY) {
+    const float w_o = eo * inv, w_p = ep * inv;
+    v = ld_nt((const f32x4*)o);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { o0[i] = p[i]; o1[i] = p[4 + i]; }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o0[i] = w_o * o0[i] + w_p * p[i];
-      o1[i] = w_o * o1[i] + w_p * p[4 + i];
-    }
+    for (int i = 0; i < 4; ++i) v[i] = w_o * v[i] + w_p * p[i];
   }
-  ((f32x4*)orow)[0] = o0;
-  ((f32x4*)orow)[1] = o1;
-  if (c == 0) a.lse[r] = nl;
+  st_nt(v, (f32x4*)o);
+  if (c == 0) a.lse[li] = nl;
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  const int64_t threads = (int64_t)a.heads * a.tokens * (a.d / 8);
+  const int64_t threads = (int64_t)a.heads * a.tokens * (a.d / 4);
   if (threads == 0) return hipSuccess;
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (a.d == 128) {
@@ -98,32 +99,31 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 
 
+// Token-major rows (the order of `out` and dO in memory), 4 elements per thread.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void delta_kernel(DeltaArgs a) {
-  constexpr int TPR = D / 8;
+  constexpr int TPR = D / 4;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t r = gid / TPR;
   const int c = (int)(gid - r * TPR);
   const bool ok = r < (int64_t)a.heads * a.tokens;
+  const int64_t t = r / a.heads;
+  const int h = (int)(r - t * a.heads);
   float acc = 0.f;
   if (ok) {
-    const int h = (int)(r / a.tokens);
-    const int64_t t = r - (int64_t)h * a.tokens;
-    const float* orow = a.out + (t * a.heads + h) * D + c * 8;
-    const char* drow = (const char*)a.dout + ((t * a.do_st + (int64_t)h * a.do_sh) + c * 8) * (BF16 ? 2 : 4);
-    float dv[8];
-    unpack8(drow, BF16, dv);
-    const f32x4 o0 = ((const f32x4*)orow)[0], o1 = ((const f32x4*)orow)[1];
+    const void* drow = (const char*)a.dout + (t * a.do_st + (int64_t)h * a.do_sh) * (BF16 ? 2 : 4);
+    const f32x4 d4 = load4<BF16>(drow, 4 * c);
+    const f32x4 o4 = ld_nt((const f32x4*)(a.out + r * D + 4 * c));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc = fmaf(dv[i], o0[i], fmaf(dv[4 + i], o1[i], acc));
+    for (int i = 0; i < 4; ++i) acc = fmaf(d4[i], o4[i], acc);
   }
 #pragma unroll
   for (int o = TPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (ok && c == 0) a.delta[r] = acc;
+  if (ok && c == 0) a.delta[(int64_t)h * a.tokens + t] = acc;
 }
 
 hipError_t launch_delta(const DeltaArgs& a, hipStream_t stream) {
-  const int64_t threads = (int64_t)a.heads * a.tokens * (a.d / 8);
+  const int64_t threads = (int64_t)a.heads * a.tokens * (a.d / 4);
   if (threads == 0) return hipSuccess;
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (a.d == 128) {
