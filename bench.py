@@ -42,6 +42,10 @@ def parse():
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a device copy of a known size (reference for HBM byte counters)")
+    p.add_argument("--write-traffic", nargs=4, metavar=("CAL_FETCH", "CAL_WRITE", "RUN_FETCH", "RUN_WRITE"),
+                   help="CPU only: turn four rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE of "
+                        "--copy-calibration, then of a --steps 2 --warmup 0 --no-extras run) into "
+                        "profiles/traffic.json for the current kernel sources")
     return p.parse_args()
 
 
@@ -90,6 +94,58 @@ def traffic_for(kernel):
     if not ent or ent.get("source_hash") != kernel_source_hash():
         return None
     return ent.get("bytes_per_launch")
+
+
+def _counter_rows(folder, counter):
+    """(kernel name, KiB) per dispatch, in dispatch order, from a rocprofv3
+    --pmc csv folder."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                name = r["Kernel_Name"]
+                name = name[5:] if name.startswith("void ") else name
+                rows.append((int(r["Dispatch_Id"]), name.rsplit("(", 1)[0], float(r["Counter_Value"])))
+    rows.sort()
+    return [(n, v) for _, n, v in rows]
+
+
+def write_traffic(cal_fetch, cal_write, run_fetch, run_write):
+    """HBM bytes per launch of the attention kernels: FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch) of one bench step, each scaled by what the same counter
+    reads for the 1 GiB device copy of --copy-calibration."""
+    import statistics
+    scales = []
+    for folder, counter in ((cal_fetch, "FETCH_SIZE"), (cal_write, "WRITE_SIZE")):
+        vals = [v for n, v in _counter_rows(folder, counter) if "copyBuffer" in n]
+        if not vals:
+            raise SystemExit(f"no device-copy dispatch with {counter} in {folder}")
+        scales.append((1 << 30) / (statistics.median(vals) * 1024))
+    rec = {"_comment": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), "
+                       f"scaled by what each counter reads for a 1 GiB device copy (bench.py --copy-calibration): "
+                       f"FETCH_SIZE x {scales[0]:.3f}, WRITE_SIZE x {scales[1]:.3f}. Workload: bench.py "
+                       "--no-cpu-baseline --no-extras --steps 2 --warmup 0 (long_tail, 4 ring steps); "
+                       "the first step's launches are listed.",
+           "read_scale": round(scales[0], 4), "write_scale": round(scales[1], 4)}
+    fetch = _counter_rows(run_fetch, "FETCH_SIZE")
+    write = _counter_rows(run_write, "WRITE_SIZE")
+    src = kernel_source_hash()
+    for name in sorted({n for n, _ in fetch if n.startswith("cpattn::")}):
+        fb = [v * 1024 * scales[0] for n, v in fetch if n == name]
+        wb = [v * 1024 * scales[1] for n, v in write if n == name]
+        per_step = max(1, len(fb) // 2)
+        fb, wb = fb[:per_step], wb[:per_step]
+        rec[name] = {"source_hash": src, "launches": per_step,
+                     "fetch_bytes_per_launch": [int(x) for x in fb],
+                     "write_bytes_per_launch": [int(x) for x in wb],
+                     "bytes_per_launch": int((sum(fb) + sum(wb)) / per_step)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(path)
 
 
 def run_hot_path(c, torch, w, steps, warmup):
@@ -258,6 +314,9 @@ def extras(c, torch):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs one rank's share "
               "on one MI355X and has no multi-GPU path.", file=sys.stderr)
@@ -289,7 +348,7 @@ def main():
     tflops = (fwd_flops + bwd_flops) / (wall_ms * 1e-3) / 1e12
 
     # dominant kernel and its roofline
-    kern = {"fwd_step": ("cpattn::fwd_bf16_kernel<128, 4, 2>", fwd_flops / w.cp),
+    kern = {"fwd_step": ("cpattn::fwd_bf16_kernel<128, 4, 1>", fwd_flops / w.cp),
             "bwd_step": ("cpattn::(anonymous namespace)::bwd_bf16_kernel<128>", bwd_flops / w.cp)}
     dom = max((k for k in kern if k in st), key=lambda k: st[k]["total_ms"])
     kname, flops_per_launch = kern[dom]
