@@ -41,6 +41,11 @@ namespace cpattn {
 // tiles.  O / l and m + log2(l) use the same m, so the result is exact.
 constexpr float kRescale = 8.0f;
 
+#ifndef CPATTN_FWD_PF
+#define CPATTN_FWD_PF 3
+#endif
+constexpr int kFwdPF = CPATTN_FWD_PF;   // K operand reads ahead of their products
+
 
 
 // Waves per SIMD the kernel is compiled for: two when each wave owns 32
@@ -128,75 +133,63 @@ void fwd_bf16_kernel(FwdArgs a) {
     const uint16_t* tk = s_k[buf];
     const uint16_t* tv = s_v[buf];
     const bool full = t0 >= sg.full_lo && t0 + BN <= sg.full_hi;
-    // S^T for the whole 64-key tile (two independent MFMA chains per query
-    // block), then one softmax update, then PV.
+    // S^T for the whole 64-key tile, then one softmax update, then PV. The
+    // two 32-key blocks of S^T run as one accumulator chain each, block 0
+    // first, so block 0's mask and partial row max are done under block 1's
+    // products. K operands are read PF products ahead; each step is fenced.
+    static_assert(QB == 1 && BN == 64, "the tile schedule covers one 32-query block and two key blocks");
+    constexpr int NK = D / 16;
     f32x16 acc_s[QB][BN / 32];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc_s[qb][kb][i] = 0.f;
-    // K operands are read four k-steps ahead of their MFMAs so the LDS
-    // latency hides behind the matrix pipe
-    constexpr int NKS = D / 16, NKB = BN / 32, PF = 4;
-    bf16x8 kop[PF][NKB];
-#pragma unroll
-    for (int ks = 0; ks < PF; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) kop[ks][kb] = read_row8<D>(tk, kb * 32, col, ks, hh);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 cur[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) cur[kb] = kop[ks % PF][kb];
-      if (ks + PF < NKS) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) kop[ks % PF][kb] = read_row8<D>(tk, kb * 32, col, ks + PF, hh);
-      }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc_s[qb][kb] = mfma32(cur[kb], qreg[qb][ks], acc_s[qb][kb]);
-    }
-    // keep that order through the machine scheduler: PF*NKB reads first,
-    // then per k-step its MFMAs followed by the reads of k-step ks + PF
-    __builtin_amdgcn_sched_group_barrier(0x100, PF * NKB, 0);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NKB * QB, 0);
-      if (ks + PF < NKS) __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
-    }
-    if (!full) {
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
+      for (int i = 0; i < 16; ++i) acc_s[0][kb][i] = 0.f;
+    auto mask_block = [&](int kb) {
+      if (!full) {
         const int kbase0 = t0 + kb * 32 + 4 * hh;     // key offset of register 0
         const int rem = sg.n - kbase0;                 // registers at offset >= rem are past the segment
         const int pbase = sg.pos + kbase0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int off = 8 * (i >> 2) + (i & 3);
-          const bool in = off < rem;
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const bool ok = in & in_ranges(kr[qb], pbase + off);
-            acc_s[qb][kb][i] = ok ? acc_s[qb][kb][i] : -INFINITY;
-          }
+          acc_s[0][kb][i] = ((off < rem) & in_ranges(kr[0], pbase + off)) ? acc_s[0][kb][i] : -INFINITY;
         }
       }
+    };
+    bf16x8 kop[2 * NK];
+    auto read_k = [&](int u) { kop[u] = read_row8<D>(tk, 32 * (u / NK), col, u % NK, hh); };
+#pragma unroll
+    for (int u = 0; u < kFwdPF; ++u) read_k(u);
+    float mx0 = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2 * NK; ++u) {
+      if (u + kFwdPF < 2 * NK) read_k(u + kFwdPF);
+      acc_s[0][u / NK] = mfma32(kop[u], qreg[0][u % NK], acc_s[0][u / NK]);
+      if (u == NK + 2) mask_block(0);
+      if (u == NK + 3)
+        mx0 = max3f(max3f(max3f(max3f(acc_s[0][0][0], acc_s[0][0][1], acc_s[0][0][2]), acc_s[0][0][3], acc_s[0][0][4]),
+                          acc_s[0][0][5], acc_s[0][0][6]), acc_s[0][0][7], acc_s[0][0][8]);
+      if (u == NK + 4)
+        mx0 = fmaxf(max3f(max3f(max3f(mx0, acc_s[0][0][9], acc_s[0][0][10]), acc_s[0][0][11], acc_s[0][0][12]),
+                          acc_s[0][0][13], acc_s[0][0][14]), acc_s[0][0][15]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (NK + 2 >= 2 * NK) mask_block(0);   // D = 64: block 1 is too short to carry them
+    if (NK + 3 >= 2 * NK)
+      mx0 = max3f(max3f(max3f(max3f(acc_s[0][0][0], acc_s[0][0][1], acc_s[0][0][2]), acc_s[0][0][3], acc_s[0][0][4]),
+                        acc_s[0][0][5], acc_s[0][0][6]), acc_s[0][0][7], acc_s[0][0][8]);
+    if (NK + 4 >= 2 * NK)
+      mx0 = fmaxf(max3f(max3f(max3f(mx0, acc_s[0][0][9], acc_s[0][0][10]), acc_s[0][0][11], acc_s[0][0][12]),
+                        acc_s[0][0][13], acc_s[0][0][14]), acc_s[0][0][15]);
+    mask_block(1);
     float mt[QB];
     bool need = false;
+    {
+      float mx = mx0;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = acc_s[qb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int i = (kb == 0 ? 1 : 0); i + 1 < 16; i += 2) mx = max3f(mx, acc_s[qb][kb][i], acc_s[qb][kb][i + 1]);
-      mx = fmaxf(mx, acc_s[qb][BN / 32 - 1][15]);
-      mt[qb] = max_halves(mx) * a.scale_log2;
-      need |= mt[qb] > m_run[qb] + kRescale;
+      for (int i = 0; i + 1 < 16; i += 2) mx = max3f(mx, acc_s[0][1][i], acc_s[0][1][i + 1]);
+      mt[0] = max_halves(mx) * a.scale_log2;
+      need |= mt[0] > m_run[0] + kRescale;
     }
     if (__any(need)) {
 #pragma unroll
