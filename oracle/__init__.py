@@ -12,7 +12,8 @@ What it follows (page titles as given at the top of each page):
   * same page, section 2 (Ring Attention paragraph): blockwise attention while
     key/value blocks stream around the ranks.
   * same page, section 4: the teacher-forcing sequence [clean history ; noisy
-    target] and what each stream may see.
+    target] and what each stream may see, and the balanced split that gives
+    every rank the clean/noisy chunks of the same time segments (tf_split.py).
   * LongVILA article (ZIGZAG-RINGATTN, "balancing compute"): the zigzag chunk
     assignment (the chunk rule itself is not printed; see zigzag.py).
   * "Speeding up Variable-Length Training with Dynamic Context Parallelism and
@@ -28,3 +29,4 @@ from .zigzag import (rank_chunks, local_rows, partition, count_pairs,  # noqa: F
                      step_source)
 from .softmax_attention import attention, attention_backward, bwd_delta, default_scale  # noqa: F401
 from .lse_merge import merge  # noqa: F401
+from . import tf_split  # noqa: F401
