@@ -261,10 +261,10 @@ def extras(c, torch):
     from context_attention_varlen_amd.ring import ForwardBuffers, RankPlan, partition
     out = {}
     gen = torch.Generator(device="cuda")
-    for name in ("packed_varlen", "long_video", "tf_dit"):
+    for name in ("packed_varlen", "long_video", "tf_dit", "tf_dit_split"):
         w = workloads.WORKLOADS[name]
         gen.manual_seed(0)
-        plan = RankPlan.make(w.cu_seqlens, w.cp, w.rank)
+        plan = RankPlan.make(w.cu_seqlens, w.cp, w.rank, tf=(w.tf_chunk, w.tf_num) if w.tf_chunk else None)
         mk = lambda h: (torch.randn((w.tokens, h, w.head_dim), device="cuda", generator=gen)  # noqa: E731
                         * w.value_scale).bfloat16()
         qg, kg, vg = mk(w.heads_q), mk(w.heads_kv), mk(w.heads_kv)
@@ -292,6 +292,27 @@ def extras(c, torch):
         tfl = 4 * w.head_dim * w.heads_q * pairs / (ms * 1e-3) / 1e12
         out[name] = {"fwd_ms": round(ms, 3), "fwd_tflops": round(tfl, 1),
                      "pct_peak": round(100 * tfl / PEAK_BF16_TFLOPS, 1), "pairs_per_head": pairs}
+        if w.backward:
+            do = partition(mk(w.heads_q), plan)
+            dq = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+            dk = torch.zeros(ks[0].shape, dtype=torch.float32, device="cuda")
+            dv = torch.zeros_like(dk)
+            delta = torch.empty((w.heads_q, q.shape[0]), dtype=torch.float32, device="cuda")
+            tb = Timer(torch)
+            for it in range(4):
+                c.cpattn_bwd_preprocess(bufs.out, do, delta)
+                for s in range(w.cp):
+                    j = (w.rank - s) % w.cp
+                    f = lambda s=s, j=j: c.cpattn_bwd_step(q, ks[j], vs[j], do, bufs.lse, delta,  # noqa: E731
+                                                           plan.cu_local_dev, plan.cu_local_dev, plan.num_seqs,
+                                                           w.mask, sts[s], 0.0, dq, dk, dv, bufs.workspace)
+                    (tb if it else (lambda n, fn: fn()))("bwd", f)
+            torch.cuda.synchronize()
+            bms = tb.stats()["bwd"]["total_ms"] / 3
+            btf = 10 * w.head_dim * w.heads_q * pairs / (bms * 1e-3) / 1e12
+            out[name].update({"bwd_ms": round(bms, 3), "bwd_tflops": round(btf, 1),
+                              "bwd_pct_peak": round(100 * btf / PEAK_BF16_TFLOPS, 1)})
+            del do, dq, dk, dv, delta
         if name == "long_video":
             # merge with every partial row live (finite lse_partial)
             bufs.lse_partial.normal_()

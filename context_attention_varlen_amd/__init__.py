@@ -26,7 +26,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTS = (
     "cpattn_version", "cpattn_status_string", "cpattn_last_hip_error", "cpattn_partition_index", "cpattn_partition",
-    "cpattn_unpartition", "cpattn_count_pairs", "cpattn_workspace_size", "cpattn_workspace_status",
+    "cpattn_unpartition", "cpattn_partition_index_tf", "cpattn_partition_tf", "cpattn_unpartition_tf",
+    "cpattn_count_pairs", "cpattn_workspace_size", "cpattn_workspace_status",
     "cpattn_fwd_step", "cpattn_merge", "cpattn_bwd_preprocess", "cpattn_bwd_step",
 )
 
@@ -70,6 +71,9 @@ def _load():
         "cpattn_partition_index": (ctypes.c_int, [P, I32, I32, I32, P, P]),
         "cpattn_partition": (ctypes.c_int, [TP, TP, P, I32, I32, I32, P]),
         "cpattn_unpartition": (ctypes.c_int, [TP, TP, P, I32, I32, I32, P]),
+        "cpattn_partition_index_tf": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P]),
+        "cpattn_partition_tf": (ctypes.c_int, [TP, TP, P, I32, I32, I32, I32, I32, P]),
+        "cpattn_unpartition_tf": (ctypes.c_int, [TP, TP, P, I32, I32, I32, I32, I32, P]),
         "cpattn_count_pairs": (I64, [P, I32, ctypes.c_int, SP]),
         "cpattn_workspace_size": (S, [I64, I64, I32]),
         "cpattn_workspace_status": (ctypes.c_int, [P, P, ctypes.POINTER(ctypes.c_int)]),
@@ -162,6 +166,36 @@ def cpattn_unpartition(src_local, dst_global, cu_seqlens_global_dev, num_seqs, c
     st = _lib.cpattn_unpartition(ctypes.byref(_tensor(src_local)), ctypes.byref(_tensor(dst_global)),
                                  _ptr(cu_seqlens_global_dev), num_seqs, cp, rank, _stream(stream))
     _check(st, "cpattn_unpartition")
+
+
+def cpattn_partition_index_tf(cu_seqlens_global, cp: int, rank: int, tf_chunk_tokens: int, tf_num_chunks: int,
+                              with_map: bool = True):
+    """Host index plan of the balanced teacher-forcing split: (cu_seqlens_local
+    int32, local_to_global int64 or None)."""
+    cu = np.ascontiguousarray(cu_seqlens_global, dtype=np.int32)
+    nseq = len(cu) - 1
+    cu_l = np.zeros(nseq + 1, np.int32)
+    l2g = np.zeros(int(cu[-1]) // cp if nseq >= 0 else 0, np.int64) if with_map else None
+    st = _lib.cpattn_partition_index_tf(cu.ctypes.data, nseq, cp, rank, tf_chunk_tokens, tf_num_chunks,
+                                        cu_l.ctypes.data, l2g.ctypes.data if l2g is not None else None)
+    _check(st, "cpattn_partition_index_tf")
+    return cu_l, l2g
+
+
+def cpattn_partition_tf(src_global, dst_local, cu_seqlens_global_dev, num_seqs, cp, rank, tf_chunk_tokens,
+                        tf_num_chunks, stream=None):
+    st = _lib.cpattn_partition_tf(ctypes.byref(_tensor(src_global)), ctypes.byref(_tensor(dst_local)),
+                                  _ptr(cu_seqlens_global_dev), num_seqs, cp, rank, tf_chunk_tokens, tf_num_chunks,
+                                  _stream(stream))
+    _check(st, "cpattn_partition_tf")
+
+
+def cpattn_unpartition_tf(src_local, dst_global, cu_seqlens_global_dev, num_seqs, cp, rank, tf_chunk_tokens,
+                          tf_num_chunks, stream=None):
+    st = _lib.cpattn_unpartition_tf(ctypes.byref(_tensor(src_local)), ctypes.byref(_tensor(dst_global)),
+                                    _ptr(cu_seqlens_global_dev), num_seqs, cp, rank, tf_chunk_tokens, tf_num_chunks,
+                                    _stream(stream))
+    _check(st, "cpattn_unpartition_tf")
 
 
 def cpattn_count_pairs(cu_seqlens_global, mask_mode, step: Step) -> int:

@@ -45,9 +45,26 @@ cpattn_status check_step(const cpattn_step* s, cpattn_mask_mode mode) {
   if (mode == CPATTN_MASK_TF_BLOCK) {
     if (s->tf_chunk_tokens <= 0 || s->tf_num_chunks <= 0) return CPATTN_ERR_INVALID_ARG;
     if ((int64_t)s->tf_chunk_tokens * s->tf_num_chunks * 2 >= kMaxRows) return CPATTN_ERR_INVALID_ARG;
-    if (s->cp != 1) return CPATTN_ERR_UNSUPPORTED;
+    // balanced split: equal time-chunk shares, and chunk blocks of at least
+    // 32 rows (the workspace's item bound)
+    if (s->cp > 1 && (s->tf_num_chunks % s->cp || s->tf_chunk_tokens < 32)) return CPATTN_ERR_INVALID_ARG;
   }
   return CPATTN_OK;
+}
+
+bool tf_split(cpattn_mask_mode mode, const cpattn_step* s) { return mode == CPATTN_MASK_TF_BLOCK && s->cp > 1; }
+
+// Items a schedule over `tokens` primary rows can produce.
+int64_t sched_items(cpattn_mask_mode mode, const cpattn_step* s, int64_t tokens, int32_t nseq, int tile) {
+  if (tf_split(mode, s))
+    return (int64_t)nseq * 2 * (s->tf_num_chunks / s->cp) * ((s->tf_chunk_tokens + tile - 1) / tile);
+  return max_items_for(tokens, nseq, tile);
+}
+
+// Mask the attention kernels apply: under the balanced teacher-forcing split
+// the scheduler hands them only fully allowed segments.
+int kernel_mask(cpattn_mask_mode mode, const cpattn_step* s) {
+  return tf_split(mode, s) ? (int)CPATTN_MASK_BIDIR : (int)mode;
 }
 
 int src_rank(const cpattn_step* s) { return ((s->rank - s->step) % s->cp + s->cp) % s->cp; }
@@ -154,8 +171,34 @@ CPATTN_API cpattn_status cpattn_partition_index(const int32_t* cu_g, int32_t nse
   return CPATTN_OK;
 }
 
+CPATTN_API cpattn_status cpattn_partition_index_tf(const int32_t* cu_g, int32_t nseq, int32_t cp, int32_t rank,
+                                                   int32_t tf_chunk_tokens, int32_t tf_num_chunks, int32_t* cu_l,
+                                                   int64_t* l2g) {
+  if (!cu_g || !cu_l || nseq < 0 || cp < 1 || rank < 0 || rank >= cp) return CPATTN_ERR_INVALID_ARG;
+  if (tf_chunk_tokens <= 0 || tf_num_chunks <= 0 || tf_num_chunks % cp || cu_g[0] != 0) return CPATTN_ERR_INVALID_ARG;
+  const int64_t B = tf_chunk_tokens, N = tf_num_chunks, m = N / cp;
+  for (int b = 0; b < nseq; ++b)
+    if ((int64_t)cu_g[b + 1] - cu_g[b] != 2 * B * N) return CPATTN_ERR_INVALID_ARG;
+  cu_l[0] = 0;
+  int64_t t = 0;
+  for (int b = 0; b < nseq; ++b) {
+    const int64_t g0 = cu_g[b];
+    for (int stream = 0; stream < 2; ++stream)
+      for (int64_t k = 0; k < m; ++k) {
+        const int64_t base = g0 + stream * B * N + (int64_t)tf_rank_chunk(rank, (int32_t)k, cp) * B;
+        for (int64_t o = 0; o < B; ++o) {
+          if (l2g) l2g[t] = base + o;
+          ++t;
+        }
+      }
+    cu_l[b + 1] = (int32_t)t;
+  }
+  return CPATTN_OK;
+}
+
 static cpattn_status partition_common(const cpattn_tensor* src, cpattn_tensor* dst, const int32_t* cu_dev,
-                                      int32_t nseq, int32_t cp, int32_t rank, void* stream, bool scatter) {
+                                      int32_t nseq, int32_t cp, int32_t rank, void* stream, bool scatter,
+                                      int32_t tf_b = 0, int32_t tf_n = 0) {
   cpattn_status st;
   if ((st = check_tensor(src)) != CPATTN_OK) return st;
   if ((st = check_tensor(dst)) != CPATTN_OK) return st;
@@ -182,6 +225,8 @@ static cpattn_status partition_common(const cpattn_tensor* src, cpattn_tensor* d
   a.cp = cp;
   a.rank = rank;
   a.scatter = scatter ? 1 : 0;
+  a.tf_b = cp > 1 ? tf_b : 0;
+  a.tf_n = cp > 1 ? tf_n : 0;
   clear_stale_error();
   return hip_status(launch_partition(a, (hipStream_t)stream));
 }
@@ -198,6 +243,22 @@ CPATTN_API cpattn_status cpattn_unpartition(const cpattn_tensor* src_local, cpat
   return partition_common(src_local, dst_global, cu_dev, nseq, cp, rank, stream, true);
 }
 
+CPATTN_API cpattn_status cpattn_partition_tf(const cpattn_tensor* src_global, cpattn_tensor* dst_local,
+                                             const int32_t* cu_dev, int32_t nseq, int32_t cp, int32_t rank,
+                                             int32_t tf_chunk_tokens, int32_t tf_num_chunks, void* stream) {
+  if (tf_chunk_tokens <= 0 || tf_num_chunks <= 0 || tf_num_chunks % (cp > 0 ? cp : 1)) return CPATTN_ERR_INVALID_ARG;
+  return partition_common(src_global, dst_local, cu_dev, nseq, cp, rank, stream, false, tf_chunk_tokens,
+                          tf_num_chunks);
+}
+
+CPATTN_API cpattn_status cpattn_unpartition_tf(const cpattn_tensor* src_local, cpattn_tensor* dst_global,
+                                               const int32_t* cu_dev, int32_t nseq, int32_t cp, int32_t rank,
+                                               int32_t tf_chunk_tokens, int32_t tf_num_chunks, void* stream) {
+  if (tf_chunk_tokens <= 0 || tf_num_chunks <= 0 || tf_num_chunks % (cp > 0 ? cp : 1)) return CPATTN_ERR_INVALID_ARG;
+  return partition_common(src_local, dst_global, cu_dev, nseq, cp, rank, stream, true, tf_chunk_tokens,
+                          tf_num_chunks);
+}
+
 CPATTN_API int64_t cpattn_count_pairs(const int32_t* cu_g, int32_t nseq, cpattn_mask_mode mode,
                                       const cpattn_step* st) {
   if (!cu_g || nseq < 0 || check_step(st, mode) != CPATTN_OK || cu_g[0] != 0) return -1;
@@ -209,7 +270,17 @@ CPATTN_API int64_t cpattn_count_pairs(const int32_t* cu_g, int32_t nseq, cpattn_
     if (mode == CPATTN_MASK_TF_BLOCK) {
       const int64_t B = st->tf_chunk_tokens, N = st->tf_num_chunks;
       if (L != 2 * B * N) return -1;
-      total += N * (N + 1) * B * B;
+      if (cp == 1) {
+        total += N * (N + 1) * B * B;
+        continue;
+      }
+      // balanced split: rank r's clean query chunk c sees source j's clean
+      // chunks <= c, its noisy chunk c sees j's clean chunks < c plus the
+      // noisy chunk c when j holds it
+      for (int32_t k = 0; k < N / cp; ++k) {
+        const int32_t c = tf_rank_chunk(r, k, cp);
+        total += B * B * (tf_count_below(j, c + 1, cp) + tf_count_below(j, c, cp) + (tf_owner(c, cp) == j ? 1 : 0));
+      }
       continue;
     }
     if (cp == 1) {
@@ -262,7 +333,8 @@ CPATTN_API cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_te
   const bool bf16 = q->dtype == CPATTN_BF16;
   const int d = q->head_dim;
   const int tile_p = fwd_tile_rows(bf16);
-  const int64_t max_items = max_items_for(q->tokens, nseq, tile_p);
+  const int64_t max_items = sched_items(mode, step, q->tokens, nseq, tile_p);
+  if (max_items > ws_item_capacity(q->tokens, nseq)) return CPATTN_ERR_INVALID_ARG;
   const SchedArgs sa = sched_args(ws, cu_q, cu_k, nseq, q->tokens, k->tokens, step, step->rank, src_rank(step),
                                   true, mode, tile_p, 64, 1, max_items, L.a);
   hipStream_t s = (hipStream_t)stream;
@@ -287,7 +359,7 @@ CPATTN_API cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_te
   a.grp = q->heads / k->heads;
   a.scale = sc;
   a.scale_log2 = sc * 1.4426950408889634f;
-  a.mask = (int)mode;
+  a.mask = kernel_mask(mode, step);
   a.tf_b = sa.tf_b;
   a.tf_n = sa.tf_n;
   a.hdr = sa.hdr;
@@ -371,12 +443,13 @@ CPATTN_API cpattn_status cpattn_bwd_step(const cpattn_tensor* q, const cpattn_te
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.hq = q->heads; a.hkv = k->heads; a.grp = grp;
   a.scale = sc; a.scale_log2 = sc * 1.4426950408889634f;
-  a.mask = (int)mode;
+  a.mask = kernel_mask(mode, step);
 
   // schedules: query tiles (dQ) in region A, key tiles (dK, dV; cost counts
   // every q-head of the group) in region B
   const int tq = bwd_dq_tile_rows(bf16), tk = bwd_dkv_tile_rows(bf16);
-  const int64_t mq = max_items_for(q->tokens, nseq, tq), mk = max_items_for(k->tokens, nseq, tk);
+  const int64_t mq = sched_items(mode, step, q->tokens, nseq, tq), mk = sched_items(mode, step, k->tokens, nseq, tk);
+  if (mq > ws_item_capacity(q->tokens, nseq) || mk > ws_item_capacity(k->tokens, nseq)) return CPATTN_ERR_INVALID_ARG;
   const SchedArgs sq = sched_args(ws, cu_q, cu_k, nseq, q->tokens, k->tokens, step, step->rank, src_rank(step),
                                   true, mode, tq, 64, 1, mq, L.a);
   const SchedArgs sk = sched_args(ws, cu_k, cu_q, nseq, k->tokens, q->tokens, step, src_rank(step), step->rank,

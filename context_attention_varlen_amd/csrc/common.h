@@ -87,8 +87,31 @@ inline int64_t max_items_for(int64_t tokens, int32_t nseq, int tile) {
   return (tokens + tile - 1) / tile + 2 * (int64_t)nseq + 1;
 }
 
+// Items one schedule region can hold: the zigzag bound at the smallest tile,
+// plus room for the balanced teacher-forcing split, whose 2N/cp chunk blocks
+// per sequence (at least 32 rows each) have a ragged tail each:
+// T/tile + T/B <= T/64 + T/32 < T/16.
+inline int64_t ws_item_capacity(int64_t tokens, int32_t nseq) {
+  return (tokens + 15) / 16 + 2 * (int64_t)nseq + 1;
+}
+
+// Balanced teacher-forcing split (see the scheduler): time chunk c belongs to
+// rank u or 2cp-1-u of its round, u = c mod 2cp; rank r's k-th chunk in
+// ascending order; and how many of rank r's chunks lie below chunk c.
+__host__ __device__ inline int32_t tf_owner(int32_t c, int32_t cp) {
+  const int32_t u = c % (2 * cp);
+  return u < cp ? u : 2 * cp - 1 - u;
+}
+__host__ __device__ inline int32_t tf_rank_chunk(int32_t r, int32_t k, int32_t cp) {
+  return (k >> 1) * 2 * cp + ((k & 1) ? 2 * cp - 1 - r : r);
+}
+__host__ __device__ inline int32_t tf_count_below(int32_t r, int32_t c, int32_t cp) {
+  const int32_t u = c % (2 * cp);
+  return 2 * (c / (2 * cp)) + (r < u ? 1 : 0) + (2 * cp - 1 - r < u ? 1 : 0);
+}
+
 inline WsRegion ws_region(size_t base, int64_t tokens, int32_t nseq) {
-  const int64_t mi = max_items_for(tokens, nseq, kMinTile);
+  const int64_t mi = ws_item_capacity(tokens, nseq);
   WsRegion r;
   r.hdr = base;
   r.items = base + 256;
@@ -183,6 +206,7 @@ struct PartArgs {
   int row_bytes;                            // head_dim * element size (multiple of 16)
   int cp, rank;
   int scatter;                              // 0: global -> local, 1: local -> global
+  int tf_b, tf_n;                           // > 0: balanced teacher-forcing split, else zigzag
 };
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);

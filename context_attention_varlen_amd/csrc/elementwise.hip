@@ -142,6 +142,10 @@ hipError_t launch_delta(const DeltaArgs& a, hipStream_t stream) {
 // 2cp-1-r).  Local row t of sequence b sits at local offset o = t - cu_l[b]
 // with cu_l[b] = cu_g[b]/cp; its global row is
 //   cu_g[b] + (o < C ? r*C + o : (2cp-1-r)*C + o - C),  C = L_b/(2cp).
+// Under the balanced teacher-forcing split ("Scaling Video Training with
+// Parallelism", section 4) local row o of a sequence is, with m = N/cp time
+// chunks per rank, row o mod B of the rank's (o/B mod m)-th time chunk in the
+// clean stream (o < mB) or the noisy stream.
 // One thread moves 16 bytes; the rows of a (token, head) are contiguous.
 // ---------------------------------------------------------------------------
 
@@ -169,9 +173,19 @@ __global__ __launch_bounds__(256) void partition_kernel(PartArgs a) {
     }
     const int64_t gb = a.cu[lo];
     const int64_t len = (int64_t)a.cu[lo + 1] - gb;
-    const int64_t C = len / (2 * a.cp);
     const int64_t o = t - gb / a.cp;
-    g = gb + (o < C ? (int64_t)a.rank * C + o : (int64_t)(2 * a.cp - 1 - a.rank) * C + (o - C));
+    if (a.tf_b > 0) {
+      // balanced teacher forcing: [clean chunks of the rank ; noisy chunks],
+      // N/cp time chunks of B rows in each stream
+      const int64_t B = a.tf_b, m = a.tf_n / a.cp;
+      const int64_t blk = o / B;
+      const bool noisy = blk >= m;
+      const int64_t c = tf_rank_chunk(a.rank, (int32_t)(noisy ? blk - m : blk), a.cp);
+      g = gb + (noisy ? B * a.tf_n : 0) + c * B + (o - blk * B);
+    } else {
+      const int64_t C = len / (2 * a.cp);
+      g = gb + (o < C ? (int64_t)a.rank * C + o : (int64_t)(2 * a.cp - 1 - a.rank) * C + (o - C));
+    }
   }
   if (g < 0 || g >= a.global_tokens) return;
   const int64_t ls = a.scatter ? t : g;   // source row

@@ -97,7 +97,8 @@ __device__ int build_segments(const SchedArgs& a, int p0, int p1, const int* cb,
     }
     return ns;
   }
-  // Teacher forcing (cp = 1: a single chunk holding the whole sequence).
+  // Teacher forcing at cp = 1 (a single chunk holding the whole sequence);
+  // cp > 1 uses the balanced split (build_item_tf).
   const int B = a.tf_b, span = a.tf_b * a.tf_n, L = 2 * span;
   const int base = cb[0];
   const bool has_clean = p0 < span, has_noisy = p1 > span;
@@ -144,6 +145,60 @@ __device__ int build_segments(const SchedArgs& a, int p0, int p1, const int* cb,
   return ns;
 }
 
+// Balanced teacher-forcing split at cp > 1 ("Scaling Video Training with
+// Parallelism", section 4, balanced SP): time chunks are dealt to ranks in
+// snake order over rounds of 2cp (tf_owner), and a rank's local rows are its
+// m = N/cp clean chunks in ascending order, then its noisy chunks in the same
+// order, B rows each.  Primary tiles never straddle a chunk block, and under
+// the teacher-forcing mask a block either sees another block completely or
+// not at all, so every segment below is fully allowed and the attention
+// kernels run it unmasked (only rows past a segment end are cut).  In local
+// block indices of the secondary rank rs:
+//   clean query of chunk c   clean blocks of chunks <= c        (a prefix)
+//   noisy query of chunk c   clean blocks of chunks < c         (a prefix)
+//                            + noisy block of chunk c if rs holds it
+//   clean key of chunk c     clean blocks of chunks >= c        (a suffix)
+//                            + noisy blocks of chunks > c       (a suffix)
+//   noisy key of chunk c     noisy block of chunk c if rs holds it
+__device__ void build_item_tf(const SchedArgs& a, int pr0, int sr0, int t_in_seq, WorkItem& it) {
+  const int cp = a.cp, B = a.tf_b, m = a.tf_n / cp, span = a.tf_b * a.tf_n;
+  const int tpb = ceil_div(B, a.tile_p);
+  const int blk = t_in_seq / tpb, t = t_in_seq - blk * tpb;
+  const bool pn = blk >= m;                                      // primary block is noisy
+  const int pc = tf_rank_chunk(a.rank_p, pn ? blk - m : blk, cp);  // its time chunk
+  it.row0 = pr0 + blk * B + t * a.tile_p;
+  it.nrows = min(a.tile_p, B - t * a.tile_p);
+  it.pos0 = (pn ? span : 0) + pc * B + t * a.tile_p;
+  const int rs = a.rank_s;
+  int ns = 0;
+  auto seg = [&](int lo, int hi) {    // local blocks [lo, hi) of rank rs
+    const int first = lo < m ? tf_rank_chunk(rs, lo, cp) * B : span + tf_rank_chunk(rs, lo - m, cp) * B;
+    Segment& g = it.seg[ns++];
+    g.row = sr0 + lo * B;
+    g.pos = first;
+    g.n = (hi - lo) * B;
+    g.full_lo = 0;
+    g.full_hi = g.n;
+  };
+  const int below = tf_count_below(rs, pc, cp);       // rs's chunks < pc
+  const int upto = tf_count_below(rs, pc + 1, cp);    // rs's chunks <= pc
+  const bool holds = tf_owner(pc, cp) == rs;
+  if (a.primary_is_q) {
+    if (!pn) {
+      if (upto > 0) seg(0, upto);
+    } else {
+      if (below > 0) seg(0, below);
+      if (holds) seg(m + below, m + below + 1);
+    }
+  } else if (!pn) {
+    if (below < m) seg(below, m);
+    if (upto < m) seg(m + upto, 2 * m);
+  } else if (holds) {
+    seg(m + below, m + below + 1);
+  }
+  it.nseg = ns;
+}
+
 __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
   __shared__ int s_err;
   __shared__ int s_wave[kThreads / 64 + 1];
@@ -165,11 +220,13 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
       bool bad = (b == 0 && (p0 != 0 || s0 != 0)) || p1 < p0 || s1 < s0 ||
                  (int64_t)p1 > a.tokens_p || (int64_t)s1 > a.tokens_s;
       const int lp = p1 - p0, ls = s1 - s0;
+      const bool tfs = a.mask == CPATTN_MASK_TF_BLOCK && cp > 1;   // balanced teacher-forcing split
       if (cp > 1) bad = bad || (lp & 1) || lp != ls;
-      if (a.mask == CPATTN_MASK_TF_BLOCK) bad = bad || lp != ls || lp != 2 * a.tf_b * a.tf_n;
+      if (a.mask == CPATTN_MASK_TF_BLOCK) bad = bad || lp != ls || lp != 2 * a.tf_b * (a.tf_n / cp);
       if (bad) atomicOr(&s_err, 1);
       if (!bad) {
-        if (cp > 1) cnt = 2 * ceil_div(lp >> 1, a.tile_p);
+        if (tfs) cnt = 2 * (a.tf_n / cp) * ceil_div(a.tf_b, a.tile_p);
+        else if (cp > 1) cnt = 2 * ceil_div(lp >> 1, a.tile_p);
         else cnt = ceil_div(lp, a.tile_p);
       }
     }
@@ -204,6 +261,19 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
     const int t_in_seq = idx - a.seq_base[b];
     const int pr0 = a.cu_p[b], lp = a.cu_p[b + 1] - pr0;
     const int sr0 = a.cu_s[b], ls = a.cu_s[b + 1] - sr0;
+    if (a.mask == CPATTN_MASK_TF_BLOCK && cp > 1) {
+      WorkItem it;
+      it.seq = b;
+      it.seg[0] = Segment{0, 0, 0, 0, 0};
+      it.seg[1] = Segment{0, 0, 0, 0, 0};
+      build_item_tf(a, pr0, sr0, t_in_seq, it);
+      int cost = 0;
+      for (int s = 0; s < it.nseg; ++s) cost += ceil_div(it.seg[s].n, a.tile_s);
+      it.cost = cost * a.cost_mult;
+      a.items[idx] = it;
+      atomicAdd(&s_bins[min(it.cost, kBins - 1)], 1);
+      continue;
+    }
     int chunk_off = 0, chunk_len = lp, t = t_in_seq;
     if (cp > 1) {
       const int half = lp >> 1, per = ceil_div(half, a.tile_p);

@@ -17,7 +17,8 @@ import numpy as np
 import torch
 
 from . import (cpattn_bwd_preprocess, cpattn_bwd_step, cpattn_fwd_step, cpattn_merge,
-               cpattn_partition, cpattn_partition_index, cpattn_workspace_size, make_step)
+               cpattn_partition, cpattn_partition_index, cpattn_partition_index_tf, cpattn_partition_tf,
+               cpattn_workspace_size, make_step)
 
 
 @dataclasses.dataclass
@@ -31,21 +32,32 @@ class RankPlan:
     cu_local_dev: torch.Tensor
     num_seqs: int
     tokens_local: int
+    tf: tuple = (0, 0)   # (B, N) for the balanced teacher-forcing split, else zigzag
 
     @staticmethod
-    def make(cu_global, cp: int, rank: int, device="cuda") -> "RankPlan":
+    def make(cu_global, cp: int, rank: int, device="cuda", tf=None) -> "RankPlan":
+        """Zigzag plan, or with tf = (B, N) and cp > 1 the balanced
+        teacher-forcing split."""
         cu_g = np.ascontiguousarray(cu_global, dtype=np.int32)
-        cu_l, _ = cpattn_partition_index(cu_g, cp, rank, with_map=False)
+        split = (int(tf[0]), int(tf[1])) if tf is not None and cp > 1 and tf[0] > 0 else (0, 0)
+        if split[0]:
+            cu_l, _ = cpattn_partition_index_tf(cu_g, cp, rank, split[0], split[1], with_map=False)
+        else:
+            cu_l, _ = cpattn_partition_index(cu_g, cp, rank, with_map=False)
         return RankPlan(cp, rank, cu_g, cu_l, torch.from_numpy(cu_g).to(device),
-                        torch.from_numpy(cu_l).to(device), len(cu_g) - 1, int(cu_l[-1]))
+                        torch.from_numpy(cu_l).to(device), len(cu_g) - 1, int(cu_l[-1]), split)
 
 
 def partition(x_global: torch.Tensor, plan: RankPlan, rank: Optional[int] = None) -> torch.Tensor:
-    """Rank's zigzag share of a global THD tensor (device gather)."""
+    """Rank's share of a global THD tensor (device gather) under the plan's
+    split."""
     r = plan.rank if rank is None else rank
     out = torch.empty((plan.tokens_local,) + tuple(x_global.shape[1:]), dtype=x_global.dtype,
                       device=x_global.device)
-    cpattn_partition(x_global, out, plan.cu_global_dev, plan.num_seqs, plan.cp, r)
+    if plan.tf[0]:
+        cpattn_partition_tf(x_global, out, plan.cu_global_dev, plan.num_seqs, plan.cp, r, plan.tf[0], plan.tf[1])
+    else:
+        cpattn_partition(x_global, out, plan.cu_global_dev, plan.num_seqs, plan.cp, r)
     return out
 
 

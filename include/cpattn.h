@@ -70,7 +70,7 @@ extern "C" {
 typedef enum {
     CPATTN_OK = 0,
     CPATTN_ERR_INVALID_ARG = 1,   /* bad pointer, size, stride, rank/step, cu_seqlens */
-    CPATTN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (dtype, head_dim, mask+cp) */
+    CPATTN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (dtype, head_dim) */
     CPATTN_ERR_WORKSPACE = 3,     /* workspace missing or too small */
     CPATTN_ERR_HIP = 4            /* a HIP runtime call or launch failed */
 } cpattn_status;
@@ -84,7 +84,9 @@ typedef enum { CPATTN_F32 = 0, CPATTN_BF16 = 1 } cpattn_dtype;
  *            section 4): each sequence is [clean history ; noisy target],
  *            N time chunks of B tokens per stream (sequence length 2*N*B).
  *            Clean chunk c sees clean chunks <= c; noisy chunk c sees clean
- *            chunks < c plus its own noisy chunk.  Only with cp = 1. */
+ *            chunks < c plus its own noisy chunk.  With cp > 1 the local
+ *            tensors follow the balanced split (cpattn_partition_tf, same
+ *            page, balanced SP): N must be a multiple of cp and B >= 32. */
 typedef enum { CPATTN_MASK_CAUSAL = 0, CPATTN_MASK_BIDIR = 1, CPATTN_MASK_TF_BLOCK = 2 } cpattn_mask_mode;
 
 /* A THD tensor view.  data: device pointer, 16-byte aligned.  stride_token
@@ -150,6 +152,32 @@ cpattn_status cpattn_unpartition(const cpattn_tensor* src_local, cpattn_tensor* 
                                  const int32_t* cu_seqlens_global_dev, int32_t num_seqs,
                                  int32_t cp, int32_t rank, void* stream);
 
+/* ---- balanced teacher-forcing split --------------------------------------
+ * "Scaling Video Training with Parallelism", section 4 (balanced SP): every
+ * rank keeps the clean and the noisy chunk of the same time segments, so the
+ * noisy (loss-carrying) targets spread evenly.  The page does not print the
+ * assignment; the rule taken here deals time chunks c = 0..N-1 to ranks in
+ * snake order over rounds of 2*cp chunks (c goes to rank u or 2cp-1-u of its
+ * round, u = c mod 2cp), which gives every rank equal teacher-forcing work
+ * when N is a multiple of 2*cp.  Rank r's local rows of a sequence are its
+ * N/cp clean chunks in ascending time order, then its noisy chunks in the
+ * same order, B rows each.  Every sequence has 2*B*N tokens
+ * (B = tf_chunk_tokens, N = tf_num_chunks, N a multiple of cp); the local
+ * cu_seqlens are the prefix sums of L_b/cp.  Arguments, copies and errors
+ * as for the zigzag functions above. */
+cpattn_status cpattn_partition_index_tf(const int32_t* cu_seqlens_global_host, int32_t num_seqs,
+                                        int32_t cp, int32_t rank, int32_t tf_chunk_tokens,
+                                        int32_t tf_num_chunks, int32_t* cu_seqlens_local_host,
+                                        int64_t* local_to_global_host);
+cpattn_status cpattn_partition_tf(const cpattn_tensor* src_global, cpattn_tensor* dst_local,
+                                  const int32_t* cu_seqlens_global_dev, int32_t num_seqs,
+                                  int32_t cp, int32_t rank, int32_t tf_chunk_tokens,
+                                  int32_t tf_num_chunks, void* stream);
+cpattn_status cpattn_unpartition_tf(const cpattn_tensor* src_local, cpattn_tensor* dst_global,
+                                    const int32_t* cu_seqlens_global_dev, int32_t num_seqs,
+                                    int32_t cp, int32_t rank, int32_t tf_chunk_tokens,
+                                    int32_t tf_num_chunks, void* stream);
+
 /* Exact number of allowed (query, key) pairs per head between rank `rank`'s
  * queries and the keys it holds at ring step `step` (host-only, closed form
  * per sequence).  This is the count behind FLOP accounting from real
@@ -173,7 +201,9 @@ cpattn_status cpattn_workspace_status(const void* workspace, void* stream, cpatt
  * Blockwise attention of rank step->rank's local queries against the K/V
  * share it holds at ring step step->step ("Scaling Video Training with
  * Parallelism", section 2, Ring Attention paragraph).  Masks are applied on
- * positions in the unsplit sequences, recovered from the zigzag rule.
+ * positions in the unsplit sequences, recovered from the zigzag rule (from
+ * the balanced split for TF_BLOCK at cp > 1, where every tile the scheduler
+ * emits is fully allowed or fully skipped).
  *   q            [Tq, Hq, d]      local queries (rank step->rank)
  *   k, v         [Tk, Hkv, d]     K/V share of rank (rank - step) mod cp
  *   cu_seqlens_q_dev, cu_seqlens_k_dev  local int32[num_seqs+1]; for cp > 1

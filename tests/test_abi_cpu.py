@@ -135,7 +135,8 @@ def test_fwd_step_rejects_bad_arguments():
     assert _fwd(_FakeTensor((64, 4, 128), bf, ptr=0x1008), kv, kv, q, st) == c.ERR_INVALID_ARG  # misaligned
     assert _fwd(q, kv, kv, q, st, cu=0) == c.ERR_INVALID_ARG                  # null cu_seqlens
     assert _fwd(q, kv, kv, q, st, mode=2) == c.ERR_INVALID_ARG                # TF without B, N
-    assert _fwd(q, kv, kv, q, c.make_step(2, 0, 0, 8, 2), mode=2) == c.ERR_UNSUPPORTED  # TF with cp > 1
+    assert _fwd(q, kv, kv, q, c.make_step(2, 0, 0, 8, 2), mode=2) == c.ERR_INVALID_ARG  # TF split, B < 32
+    assert _fwd(q, kv, kv, q, c.make_step(4, 0, 0, 64, 6), mode=2) == c.ERR_INVALID_ARG  # TF split, N % cp
     assert _fwd(q, kv, kv, q, st, mode=7) == c.ERR_INVALID_ARG                # unknown mask
     small_ws = _FakeTensor((1, 1, 1), None, ptr=0x4000)
     small_ws.numel = lambda: 16
@@ -148,3 +149,43 @@ def test_workspace_size_monotone():
     a = c.cpattn_workspace_size(1024, 1024, 4)
     b = c.cpattn_workspace_size(32768, 32768, 4)
     assert 0 < a < b and b % 256 == 0
+
+
+@pytest.mark.parametrize("nseq,B,N,cp", [(1, 32, 4, 2), (3, 33, 6, 3), (2, 40, 12, 4), (1, 64, 12, 6), (2, 32, 8, 1)])
+def test_partition_index_tf_matches_oracle(nseq, B, N, cp):
+    """Balanced teacher-forcing split: host index plan bit-exact against the
+    oracle's own split (cp = 1 is the identity)."""
+    cu = np.arange(nseq + 1, dtype=np.int32) * (2 * B * N)
+    for r in range(cp):
+        cu_l, l2g = c.cpattn_partition_index_tf(cu, cp, r, B, N)
+        cu_o, l2g_o, _, _ = oracle.tf_split.local_rows(cu, cp, r, B, N)
+        assert np.array_equal(cu_l, cu_o)
+        assert np.array_equal(l2g, l2g_o)
+
+
+def test_count_pairs_tf_split_matches_oracle():
+    B, N = 32, 12
+    cu = np.array([0, 2 * B * N, 4 * B * N], np.int32)
+    for cp in (2, 3, 4, 6):
+        for r in range(cp):
+            for s in range(cp):
+                st = c.make_step(cp, r, s, B, N)
+                assert c.cpattn_count_pairs(cu, oracle.TF_BLOCK, st) == oracle.tf_split.count_pairs(cu, cp, r, s, B, N)
+    # every rank's total is N(N+1)B^2/cp per sequence when N is a multiple of 2*cp
+    for cp in (2, 3, 6):
+        for r in range(cp):
+            tot = sum(c.cpattn_count_pairs(cu, oracle.TF_BLOCK, c.make_step(cp, r, s, B, N)) for s in range(cp))
+            assert tot == 2 * N * (N + 1) * B * B // cp
+
+
+def test_tf_split_rejects_bad_input():
+    cu = np.array([0, 2 * 32 * 6], np.int32)
+    with pytest.raises(c.CpattnError):
+        c.cpattn_partition_index_tf(cu, 4, 0, 32, 6)          # 6 chunks over 4 ranks
+    with pytest.raises(c.CpattnError):
+        c.cpattn_partition_index_tf(cu, 2, 0, 32, 5)          # length is not 2*B*N
+    with pytest.raises(c.CpattnError):
+        c.cpattn_count_pairs(cu, oracle.TF_BLOCK, c.make_step(4, 0, 0, 32, 6))
+    small = np.array([0, 2 * 16 * 4], np.int32)
+    with pytest.raises(c.CpattnError):                        # chunk blocks below 32 rows at cp > 1
+        c.cpattn_count_pairs(small, oracle.TF_BLOCK, c.make_step(2, 0, 0, 16, 4))

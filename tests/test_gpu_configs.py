@@ -66,7 +66,7 @@ def _oracle_rows(w, x, r, rows, step=None):
 def _gpu_ring(w, x, r, keep=False, backward=False):
     from context_attention_varlen_amd.ring import RankPlan, partition, ring_backward, ring_forward
     td = tdtype(w.dtype)
-    plan = RankPlan.make(w.cu_seqlens, w.cp, r)
+    plan = RankPlan.make(w.cu_seqlens, w.cp, r, tf=(w.tf_chunk, w.tf_num) if w.tf_chunk else None)
     q = partition(torch.from_numpy(x["q"]).to(td).cuda(), plan)
     kg = torch.from_numpy(x["k"]).to(td).cuda()
     vg = torch.from_numpy(x["v"]).to(td).cuda()
@@ -189,3 +189,41 @@ def test_long_tail_forward_backward(cpa):
         scale = float(do_loc[rs].double().norm()) / np.sqrt(w.head_dim * w.heads_kv)
         assert float((dv_sum - want).abs().max()) <= 1e-2 * max(1.0, scale), b
         assert float(dk_sum.abs().max()) <= 1e-2 * max(1.0, scale), b
+
+
+def test_tf_dit_split_sampled(cpa):
+    """Teacher-forced DiT under the balanced split, cp = 3, rank 0 (time
+    chunks 0, 5, 6, 11; 24960 local rows): merged forward and dQ on rows
+    stratified over both streams and every chunk edge; the gradient sums
+    over every key row (sum_j dV_j = sum_i dO_i, sum_j dK_j = 0 per head)."""
+    from oracle import tf_split
+    w = workloads.WORKLOADS["tf_dit_split"]
+    x = workloads.draw(w)
+    r = 0
+    plan, bufs, _, grads = _gpu_ring(w, x, r, backward=True)
+    dq, dk, dv, _ = grads
+    B, N, cu = w.tf_chunk, w.tf_num, w.cu_seqlens
+    _, l2g, qpos, qseq = tf_split.local_rows(cu, w.cp, r, B, N)
+    m = N // w.cp
+    edges = []
+    for blk in range(2 * m):
+        edges += [blk * B, blk * B + 1, blk * B + B - 1]
+    rng = np.random.default_rng(1005)
+    rows = workloads.sample_rows(rng, len(l2g), 32, edges)
+    seq, pos = _seq_pos(cu)
+    o_ref, l_ref = oracle.attention(x["q"][l2g[rows]], x["k"], x["v"], qseq[rows], qpos[rows], seq, pos,
+                                    oracle.TF_BLOCK, tf_chunk=B, tf_num=N)
+    t = torch.from_numpy(rows).cuda()
+    check_out(bufs.out[t].cpu().numpy(), o_ref, "bf16")
+    check_lse(bufs.lse[:, t].cpu().numpy(), l_ref)
+    delta = oracle.bwd_delta(o_ref, x["dout"][l2g[rows]])
+    dq_ref, _, _ = oracle.attention_backward(x["q"][l2g[rows]], x["k"], x["v"], x["dout"][l2g[rows]], l_ref, delta,
+                                             qseq[rows], qpos[rows], seq, pos, oracle.TF_BLOCK, tf_chunk=B, tf_num=N)
+    assert rel_rms(dq[t].cpu().numpy(), dq_ref) <= TOL_GRAD_RELRMS
+    do_loc = torch.from_numpy(x["dout"][l2g]).cuda().double()
+    dv_sum = sum(dv[j].double().sum(0) for j in range(w.cp))
+    dk_sum = sum(dk[j].double().sum(0) for j in range(w.cp))
+    want = do_loc.sum(0)
+    scale = float(do_loc.norm()) / np.sqrt(w.head_dim * w.heads_kv)
+    assert float((dv_sum - want).abs().max()) <= 1e-2 * max(1.0, scale)
+    assert float(dk_sum.abs().max()) <= 1e-2 * max(1.0, scale)

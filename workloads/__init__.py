@@ -20,6 +20,9 @@ Workloads (the five shapes the library is measured and checked on):
                 with lengths uniform over multiples of 8 in [256, 2048];
                 causal, zigzag cp=4 on every sequence, Hq=32/Hkv=8, d=128,
                 bf16 q/k/v/dO N(0,1); forward and backward.
+  tf_dit_split  the tf_dit sequence under the balanced teacher-forcing split
+                over cp=3 ranks (4 time chunks per rank, 24960 local tokens),
+                rank 0; forward and backward.
 
 Page context: the long-tail length mix stands in for the variable-length
 datasets of "Speeding up Variable-Length Training with Dynamic Context
@@ -132,6 +135,8 @@ WORKLOADS = {
                        tf_chunk=3120, tf_num=12),
     "long_tail": Workload("long_tail", _c5_lengths(), 32, 8, 128, "bf16", CAUSAL, 4, 0,
                           backward=True),
+    "tf_dit_split": Workload("tf_dit_split", (74880,), 24, 24, 128, "bf16", TF_BLOCK, 3, 0,
+                             tf_chunk=3120, tf_num=12, backward=True),
 }
 
 
