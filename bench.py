@@ -330,6 +330,23 @@ def extras(c, torch):
                 "pct_peak_hbm": round(100 * nbytes / (mst["avg_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 1)}
         del q, ks, vs, bufs
         torch.cuda.empty_cache()
+    # Ulysses sequence->head exchange on one device: 4-way group over the
+    # long-video sequence (262144 tokens, 28 q-heads -> 7 per member), the
+    # shards in HBM, one member's gather of its head group
+    n, T, H, d = 4, 262144, 28, 128
+    shards = [torch.randn((T // n, H, d), device="cuda", generator=gen).bfloat16() for _ in range(n)]
+    dst = torch.empty((T, H // n, d), dtype=torch.bfloat16, device="cuda")
+    tm = Timer(torch)
+    for it in range(6):
+        (tm if it else (lambda nm, fn: fn()))("gather", lambda: c.cpattn_seq_to_head(shards, 1, dst))
+    torch.cuda.synchronize()
+    gms = tm.stats()["gather"]["avg_ms"]
+    nbytes = 2 * T * (H // n) * d * 2
+    out["ulysses_seq_to_head_long_video"] = {
+        "avg_ms": round(gms, 4), "bytes": nbytes, "gbps": round(nbytes / (gms * 1e-3) / 1e9, 1),
+        "pct_peak_hbm": round(100 * nbytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 1)}
+    del shards, dst
+    torch.cuda.empty_cache()
     return out
 
 

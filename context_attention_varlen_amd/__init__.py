@@ -27,6 +27,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 EXPORTS = (
     "cpattn_version", "cpattn_status_string", "cpattn_last_hip_error", "cpattn_partition_index", "cpattn_partition",
     "cpattn_unpartition", "cpattn_partition_index_tf", "cpattn_partition_tf", "cpattn_unpartition_tf",
+    "cpattn_seq_to_head", "cpattn_head_to_seq",
     "cpattn_count_pairs", "cpattn_workspace_size", "cpattn_workspace_status",
     "cpattn_fwd_step", "cpattn_merge", "cpattn_bwd_preprocess", "cpattn_bwd_step",
 )
@@ -74,6 +75,8 @@ def _load():
         "cpattn_partition_index_tf": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P]),
         "cpattn_partition_tf": (ctypes.c_int, [TP, TP, P, I32, I32, I32, I32, I32, P]),
         "cpattn_unpartition_tf": (ctypes.c_int, [TP, TP, P, I32, I32, I32, I32, I32, P]),
+        "cpattn_seq_to_head": (ctypes.c_int, [TP, I32, I32, TP, P]),
+        "cpattn_head_to_seq": (ctypes.c_int, [TP, I32, I32, TP, P]),
         "cpattn_count_pairs": (I64, [P, I32, ctypes.c_int, SP]),
         "cpattn_workspace_size": (S, [I64, I64, I32]),
         "cpattn_workspace_status": (ctypes.c_int, [P, P, ctypes.POINTER(ctypes.c_int)]),
@@ -196,6 +199,21 @@ def cpattn_unpartition_tf(src_local, dst_global, cu_seqlens_global_dev, num_seqs
                                     _ptr(cu_seqlens_global_dev), num_seqs, cp, rank, tf_chunk_tokens, tf_num_chunks,
                                     _stream(stream))
     _check(st, "cpattn_unpartition_tf")
+
+
+def cpattn_seq_to_head(shards, group, gathered, stream=None):
+    """Head group `group` of every shard (list of [T_s, H, d] tensors, rank
+    order) into gathered [sum T_s, H/len(shards), d]."""
+    arr = (Tensor * len(shards))(*[_tensor(t) for t in shards])
+    st = _lib.cpattn_seq_to_head(arr, len(shards), group, ctypes.byref(_tensor(gathered)), _stream(stream))
+    _check(st, "cpattn_seq_to_head")
+
+
+def cpattn_head_to_seq(gathered, group, shards, stream=None):
+    """Inverse of cpattn_seq_to_head: writes head group `group` back into the shards."""
+    arr = (Tensor * len(shards))(*[_tensor(t) for t in shards])
+    st = _lib.cpattn_head_to_seq(ctypes.byref(_tensor(gathered)), len(shards), group, arr, _stream(stream))
+    _check(st, "cpattn_head_to_seq")
 
 
 def cpattn_count_pairs(cu_seqlens_global, mask_mode, step: Step) -> int:

@@ -259,6 +259,58 @@ CPATTN_API cpattn_status cpattn_unpartition_tf(const cpattn_tensor* src_local, c
                           tf_num_chunks);
 }
 
+// Shared checks and launches of the Ulysses exchange: shard s's rows sit at
+// row offset sum_{s' < s} tokens(s') of the gathered tensor.
+static cpattn_status ulysses_common(const cpattn_tensor* shards, int32_t n, int32_t group, const cpattn_tensor* g,
+                                    void* stream, bool to_head) {
+  cpattn_status st;
+  if (!shards || !g || n < 1 || group < 0 || group >= n) return CPATTN_ERR_INVALID_ARG;
+  if ((st = check_tensor(g)) != CPATTN_OK) return st;
+  int64_t rows = 0;
+  for (int s = 0; s < n; ++s) {
+    if ((st = check_tensor(&shards[s])) != CPATTN_OK) return st;
+    if (shards[s].dtype != g->dtype || shards[s].head_dim != g->head_dim || shards[s].heads != (int64_t)g->heads * n)
+      return CPATTN_ERR_INVALID_ARG;
+    rows += shards[s].tokens;
+  }
+  if (rows > g->tokens) return CPATTN_ERR_INVALID_ARG;
+  const int es = elem_size(g->dtype);
+  clear_stale_error();
+  int64_t row0 = 0;
+  for (int s = 0; s < n; ++s) {
+    const cpattn_tensor& sh = shards[s];
+    HeadCopyArgs a;
+    const cpattn_tensor* src = to_head ? &sh : g;
+    const cpattn_tensor* dst = to_head ? g : &sh;
+    a.src = (const char*)src->data;
+    a.dst = (char*)dst->data;
+    a.src_st = src->stride_token * es;
+    a.src_sh = src->stride_head * es;
+    a.dst_st = dst->stride_token * es;
+    a.dst_sh = dst->stride_head * es;
+    a.src_row0 = to_head ? 0 : row0;
+    a.dst_row0 = to_head ? row0 : 0;
+    a.tokens = sh.tokens;
+    a.src_h0 = to_head ? group * g->heads : 0;
+    a.dst_h0 = to_head ? 0 : group * g->heads;
+    a.heads = g->heads;
+    a.row_bytes = g->head_dim * es;
+    if ((st = hip_status(launch_head_copy(a, (hipStream_t)stream))) != CPATTN_OK) return st;
+    row0 += sh.tokens;
+  }
+  return CPATTN_OK;
+}
+
+CPATTN_API cpattn_status cpattn_seq_to_head(const cpattn_tensor* shards, int32_t n_shards, int32_t group,
+                                            cpattn_tensor* gathered, void* stream) {
+  return ulysses_common(shards, n_shards, group, gathered, stream, true);
+}
+
+CPATTN_API cpattn_status cpattn_head_to_seq(const cpattn_tensor* gathered, int32_t n_shards, int32_t group,
+                                            cpattn_tensor* shards, void* stream) {
+  return ulysses_common(shards, n_shards, group, gathered, stream, false);
+}
+
 CPATTN_API int64_t cpattn_count_pairs(const int32_t* cu_g, int32_t nseq, cpattn_mask_mode mode,
                                       const cpattn_step* st) {
   if (!cu_g || nseq < 0 || check_step(st, mode) != CPATTN_OK || cu_g[0] != 0) return -1;

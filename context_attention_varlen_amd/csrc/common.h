@@ -219,6 +219,19 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_delta(const DeltaArgs& a, hipStream_t stream);
 hipError_t launch_partition(const PartArgs& a, hipStream_t stream);
 
+// Copy of `tokens` rows x `heads` heads between two THD tensors, starting at
+// (src_row0, src_h0) and (dst_row0, dst_h0): the one-device form of the
+// Ulysses sequence<->head exchange.
+struct HeadCopyArgs {
+  const char* src;
+  char* dst;
+  int64_t src_st, src_sh, dst_st, dst_sh;   // strides in bytes
+  int64_t src_row0, dst_row0, tokens;
+  int src_h0, dst_h0, heads;
+  int row_bytes;                            // head_dim * element size (multiple of 16)
+};
+hipError_t launch_head_copy(const HeadCopyArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------

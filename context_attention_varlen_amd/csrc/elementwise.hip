@@ -201,4 +201,31 @@ hipError_t launch_partition(const PartArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Ulysses sequence <-> head exchange on one device ("Scaling Video Training
+// with Parallelism", SP landscape: DeepSpeed-Ulysses shards the sequence and
+// exchanges all-to-all around attention so that every member holds all
+// tokens of a head group).  With the shards resident, each shard's block of
+// rows moves as one strided copy; one thread moves 16 bytes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void head_copy_kernel(HeadCopyArgs a) {
+  const int cpr = a.row_bytes >> 4;
+  const int64_t per_tok = (int64_t)cpr * a.heads;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = gid / per_tok;
+  if (t >= a.tokens) return;
+  const int64_t rem = gid - t * per_tok;
+  const int h = (int)(rem / cpr);
+  const int c = (int)(rem - (int64_t)h * cpr);
+  const u32x4 v = ld_nt((const u32x4*)(a.src + (a.src_row0 + t) * a.src_st + (int64_t)(a.src_h0 + h) * a.src_sh + c * 16));
+  st_nt(v, (u32x4*)(a.dst + (a.dst_row0 + t) * a.dst_st + (int64_t)(a.dst_h0 + h) * a.dst_sh + c * 16));
+}
+
+hipError_t launch_head_copy(const HeadCopyArgs& a, hipStream_t stream) {
+  const int64_t threads = a.tokens * a.heads * (a.row_bytes >> 4);
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(head_copy_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace cpattn

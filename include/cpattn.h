@@ -178,6 +178,27 @@ cpattn_status cpattn_unpartition_tf(const cpattn_tensor* src_local, cpattn_tenso
                                     int32_t cp, int32_t rank, int32_t tf_chunk_tokens,
                                     int32_t tf_num_chunks, void* stream);
 
+/* ---- Ulysses sequence <-> head exchange ------------------------------------
+ * "Scaling Video Training with Parallelism", SP landscape (DeepSpeed-Ulysses;
+ * USP / LoongTrain 2D-Attention): Ulysses shards the sequence and exchanges
+ * all-to-all around attention, so that member g of an n-way group holds all
+ * tokens of head group g (heads [g*H/n, (g+1)*H/n)); the head count must
+ * divide by n.  With every shard on one device the exchange is a gather:
+ *   shards        array of n_shards THD views [T_s, H, d], in rank order
+ *                 (contiguous token ranges of the packed batch)
+ *   gathered      [>= sum T_s, H/n_shards, d]; rows of shard s start at row
+ *                 sum_{s'<s} T_s'
+ *   group         head group g in [0, n_shards)
+ * cpattn_seq_to_head copies the shards' head group g into `gathered`;
+ * cpattn_head_to_seq writes it back (the exchange after attention), leaving
+ * the shards' other heads untouched.  dtype and head_dim must match.  Bytes
+ * are copied bit-exact, one strided copy per shard on `stream`.  Attention
+ * on the gathered tensors is cpattn_fwd_step / cpattn_bwd_step with cp = 1. */
+cpattn_status cpattn_seq_to_head(const cpattn_tensor* shards, int32_t n_shards, int32_t group,
+                                 cpattn_tensor* gathered, void* stream);
+cpattn_status cpattn_head_to_seq(const cpattn_tensor* gathered, int32_t n_shards, int32_t group,
+                                 cpattn_tensor* shards, void* stream);
+
 /* Exact number of allowed (query, key) pairs per head between rank `rank`'s
  * queries and the keys it holds at ring step `step` (host-only, closed form
  * per sequence).  This is the count behind FLOP accounting from real

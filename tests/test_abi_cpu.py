@@ -189,3 +189,21 @@ def test_tf_split_rejects_bad_input():
     small = np.array([0, 2 * 16 * 4], np.int32)
     with pytest.raises(c.CpattnError):                        # chunk blocks below 32 rows at cp > 1
         c.cpattn_count_pairs(small, oracle.TF_BLOCK, c.make_step(2, 0, 0, 16, 4))
+
+
+def _s2h(shards, group, dst):
+    import context_attention_varlen_amd as m
+    arr = (m.Tensor * len(shards))(*[m._tensor(t) for t in shards])
+    return m._lib.cpattn_seq_to_head(arr, len(shards), group, ctypes.byref(m._tensor(dst)), None)
+
+
+def test_ulysses_exchange_rejects_bad_input():
+    import torch
+    bf = torch.bfloat16
+    sh = [_FakeTensor((64, 6, 128), bf, ptr=0x10000 + 0x100000 * i) for i in range(4)]
+    dst = _FakeTensor((256, 2, 128), bf, ptr=0x900000)
+    assert _s2h(sh, 0, dst) == c.ERR_INVALID_ARG                           # 6 heads, 4 groups
+    assert _s2h(sh[:3], 3, dst) == c.ERR_INVALID_ARG                       # group out of range
+    assert _s2h(sh[:3], 0, _FakeTensor((100, 2, 128), bf, ptr=0x900000)) == c.ERR_INVALID_ARG  # too few rows
+    assert _s2h(sh[:3], 0, _FakeTensor((192, 2, 64), bf, ptr=0x900000)) == c.ERR_INVALID_ARG   # head_dim differs
+    assert _s2h([], 0, dst) == c.ERR_INVALID_ARG                           # no shards
