@@ -16,6 +16,8 @@ What it follows (page titles as given at the top of each page):
     every rank the clean/noisy chunks of the same time segments (tf_split.py).
   * same page, SP landscape (DeepSpeed-Ulysses, USP / LoongTrain): the
     sequence-to-head all-to-all, on one device a gather (ulysses.py).
+  * LongCat-Video context-parallel page: the height/width token split with a
+    near-square choice of factors (hw_split.py).
   * LongVILA article (ZIGZAG-RINGATTN, "balancing compute"): the zigzag chunk
     assignment (the chunk rule itself is not printed; see zigzag.py).
   * "Speeding up Variable-Length Training with Dynamic Context Parallelism and
@@ -31,4 +33,4 @@ from .zigzag import (rank_chunks, local_rows, partition, count_pairs,  # noqa: F
                      step_source)
 from .softmax_attention import attention, attention_backward, bwd_delta, default_scale  # noqa: F401
 from .lse_merge import merge  # noqa: F401
-from . import tf_split, ulysses  # noqa: F401
+from . import hw_split, tf_split, ulysses  # noqa: F401
