@@ -346,6 +346,25 @@ def extras(c, torch):
         "avg_ms": round(gms, 4), "bytes": nbytes, "gbps": round(nbytes / (gms * 1e-3) / 1e9, 1),
         "pct_peak_hbm": round(100 * nbytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 1)}
     del shards, dst
+    # height/width split of a video latent (31 frames x 30 x 52 tokens,
+    # 24 heads): one rank's gather at cp = 8 (2 x 4 grid)
+    frames, Hh, Ww, cp = 31, 30, 52, 8
+    split = c.cpattn_split_hw(Hh, Ww, cp)
+    Tv = frames * Hh * Ww
+    src = torch.randn((Tv, 24, d), device="cuda", generator=gen).bfloat16()
+    loc = torch.empty((Tv // cp, 24, d), dtype=torch.bfloat16, device="cuda")
+    cu_dev = torch.tensor([0, Tv], dtype=torch.int32, device="cuda")
+    tm = Timer(torch)
+    for it in range(6):
+        (tm if it else (lambda nm, fn: fn()))("hw", lambda: c.cpattn_partition_hw(src, loc, cu_dev, 1, frames, Hh, Ww,
+                                                                                   split, 3))
+    torch.cuda.synchronize()
+    hms = tm.stats()["hw"]["avg_ms"]
+    nbytes = 2 * (Tv // cp) * 24 * d * 2
+    out["hw_split_partition_video_latent"] = {
+        "split": list(split), "avg_ms": round(hms, 4), "bytes": nbytes, "gbps": round(nbytes / (hms * 1e-3) / 1e9, 1),
+        "pct_peak_hbm": round(100 * nbytes / (hms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 1)}
+    del src, loc
     torch.cuda.empty_cache()
     return out
 

@@ -27,7 +27,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 EXPORTS = (
     "cpattn_version", "cpattn_status_string", "cpattn_last_hip_error", "cpattn_partition_index", "cpattn_partition",
     "cpattn_unpartition", "cpattn_partition_index_tf", "cpattn_partition_tf", "cpattn_unpartition_tf",
-    "cpattn_seq_to_head", "cpattn_head_to_seq",
+    "cpattn_seq_to_head", "cpattn_head_to_seq", "cpattn_split_hw", "cpattn_partition_index_hw",
+    "cpattn_partition_hw", "cpattn_unpartition_hw",
     "cpattn_count_pairs", "cpattn_workspace_size", "cpattn_workspace_status",
     "cpattn_fwd_step", "cpattn_merge", "cpattn_bwd_preprocess", "cpattn_bwd_step",
 )
@@ -76,6 +77,10 @@ def _load():
         "cpattn_partition_tf": (ctypes.c_int, [TP, TP, P, I32, I32, I32, I32, I32, P]),
         "cpattn_unpartition_tf": (ctypes.c_int, [TP, TP, P, I32, I32, I32, I32, I32, P]),
         "cpattn_seq_to_head": (ctypes.c_int, [TP, I32, I32, TP, P]),
+        "cpattn_split_hw": (ctypes.c_int, [I32, I32, I32, P, P]),
+        "cpattn_partition_index_hw": (ctypes.c_int, [P, I32, I32, I32, I32, I32, I32, I32, P, P]),
+        "cpattn_partition_hw": (ctypes.c_int, [TP, TP, P, I32, I32, I32, I32, I32, I32, I32, P]),
+        "cpattn_unpartition_hw": (ctypes.c_int, [TP, TP, P, I32, I32, I32, I32, I32, I32, I32, P]),
         "cpattn_head_to_seq": (ctypes.c_int, [TP, I32, I32, TP, P]),
         "cpattn_count_pairs": (I64, [P, I32, ctypes.c_int, SP]),
         "cpattn_workspace_size": (S, [I64, I64, I32]),
@@ -199,6 +204,42 @@ def cpattn_unpartition_tf(src_local, dst_global, cu_seqlens_global_dev, num_seqs
                                     _ptr(cu_seqlens_global_dev), num_seqs, cp, rank, tf_chunk_tokens, tf_num_chunks,
                                     _stream(stream))
     _check(st, "cpattn_unpartition_tf")
+
+
+def cpattn_split_hw(H, W, cp):
+    """(split_h, split_w): the even height/width split of cp closest to square tiles."""
+    sh, sw = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(_lib.cpattn_split_hw(H, W, cp, ctypes.byref(sh), ctypes.byref(sw)), "cpattn_split_hw")
+    return sh.value, sw.value
+
+
+def cpattn_partition_index_hw(cu_seqlens_global, frames, H, W, split, rank, with_map: bool = True):
+    """Host index plan of the height/width split: (cu_seqlens_local, local_to_global or None)."""
+    cu = np.ascontiguousarray(cu_seqlens_global, dtype=np.int32)
+    nseq = len(cu) - 1
+    cp = split[0] * split[1]
+    cu_l = np.zeros(nseq + 1, np.int32)
+    l2g = np.zeros(int(cu[-1]) // cp if nseq >= 0 else 0, np.int64) if with_map else None
+    st = _lib.cpattn_partition_index_hw(cu.ctypes.data, nseq, frames, H, W, split[0], split[1], rank,
+                                        cu_l.ctypes.data, l2g.ctypes.data if l2g is not None else None)
+    _check(st, "cpattn_partition_index_hw")
+    return cu_l, l2g
+
+
+def cpattn_partition_hw(src_global, dst_local, cu_seqlens_global_dev, num_seqs, frames, H, W, split, rank,
+                        stream=None):
+    st = _lib.cpattn_partition_hw(ctypes.byref(_tensor(src_global)), ctypes.byref(_tensor(dst_local)),
+                                  _ptr(cu_seqlens_global_dev), num_seqs, frames, H, W, split[0], split[1], rank,
+                                  _stream(stream))
+    _check(st, "cpattn_partition_hw")
+
+
+def cpattn_unpartition_hw(src_local, dst_global, cu_seqlens_global_dev, num_seqs, frames, H, W, split, rank,
+                          stream=None):
+    st = _lib.cpattn_unpartition_hw(ctypes.byref(_tensor(src_local)), ctypes.byref(_tensor(dst_global)),
+                                    _ptr(cu_seqlens_global_dev), num_seqs, frames, H, W, split[0], split[1], rank,
+                                    _stream(stream))
+    _check(st, "cpattn_unpartition_hw")
 
 
 def cpattn_seq_to_head(shards, group, gathered, stream=None):

@@ -198,7 +198,7 @@ CPATTN_API cpattn_status cpattn_partition_index_tf(const int32_t* cu_g, int32_t 
 
 static cpattn_status partition_common(const cpattn_tensor* src, cpattn_tensor* dst, const int32_t* cu_dev,
                                       int32_t nseq, int32_t cp, int32_t rank, void* stream, bool scatter,
-                                      int32_t tf_b = 0, int32_t tf_n = 0) {
+                                      int32_t tf_b = 0, int32_t tf_n = 0, const int32_t* hw = nullptr) {
   cpattn_status st;
   if ((st = check_tensor(src)) != CPATTN_OK) return st;
   if ((st = check_tensor(dst)) != CPATTN_OK) return st;
@@ -227,6 +227,13 @@ static cpattn_status partition_common(const cpattn_tensor* src, cpattn_tensor* d
   a.scatter = scatter ? 1 : 0;
   a.tf_b = cp > 1 ? tf_b : 0;
   a.tf_n = cp > 1 ? tf_n : 0;
+  a.hw_h = a.hw_w = a.hw_sh = a.hw_sw = 0;
+  if (hw && cp > 1) {
+    a.hw_h = hw[0];
+    a.hw_w = hw[1];
+    a.hw_sh = hw[2];
+    a.hw_sw = hw[3];
+  }
   clear_stale_error();
   return hip_status(launch_partition(a, (hipStream_t)stream));
 }
@@ -311,6 +318,73 @@ CPATTN_API cpattn_status cpattn_head_to_seq(const cpattn_tensor* gathered, int32
   return ulysses_common(shards, n_shards, group, gathered, stream, false);
 }
 
+// ---- height/width split (LongCat-Video context-parallel page) -------------
+static bool hw_valid(int32_t frames, int32_t H, int32_t W, int32_t sh, int32_t sw) {
+  return frames > 0 && H > 0 && W > 0 && sh > 0 && sw > 0 && H % sh == 0 && W % sw == 0 &&
+         (int64_t)frames * H * W < kMaxRows;
+}
+
+CPATTN_API cpattn_status cpattn_split_hw(int32_t H, int32_t W, int32_t cp, int32_t* split_h, int32_t* split_w) {
+  if (H <= 0 || W <= 0 || cp < 1 || !split_h || !split_w) return CPATTN_ERR_INVALID_ARG;
+  int best_h = 0;
+  double best = 0.0;
+  for (int a = 1; a <= cp; ++a) {
+    if (cp % a || H % a || W % (cp / a)) continue;
+    const double d = std::fabs((double)H / a - (double)W / (cp / a));
+    if (best_h == 0 || d < best) {   // ascending a: ties keep the smaller height split
+      best_h = a;
+      best = d;
+    }
+  }
+  if (best_h == 0) return CPATTN_ERR_INVALID_ARG;
+  *split_h = best_h;
+  *split_w = cp / best_h;
+  return CPATTN_OK;
+}
+
+CPATTN_API cpattn_status cpattn_partition_index_hw(const int32_t* cu_g, int32_t nseq, int32_t frames, int32_t H,
+                                                   int32_t W, int32_t split_h, int32_t split_w, int32_t rank,
+                                                   int32_t* cu_l, int64_t* l2g) {
+  if (!cu_g || !cu_l || nseq < 0 || !hw_valid(frames, H, W, split_h, split_w) || cu_g[0] != 0)
+    return CPATTN_ERR_INVALID_ARG;
+  const int32_t cp = split_h * split_w;
+  if (rank < 0 || rank >= cp) return CPATTN_ERR_INVALID_ARG;
+  const int64_t L = (int64_t)frames * H * W, th = H / split_h, tw = W / split_w;
+  const int64_t rh = rank / split_w, rw = rank % split_w;
+  for (int b = 0; b < nseq; ++b)
+    if ((int64_t)cu_g[b + 1] - cu_g[b] != L) return CPATTN_ERR_INVALID_ARG;
+  cu_l[0] = 0;
+  int64_t t = 0;
+  for (int b = 0; b < nseq; ++b) {
+    for (int64_t f = 0; f < frames; ++f)
+      for (int64_t h = rh * th; h < (rh + 1) * th; ++h)
+        for (int64_t w = rw * tw; w < (rw + 1) * tw; ++w) {
+          if (l2g) l2g[t] = cu_g[b] + (f * H + h) * W + w;
+          ++t;
+        }
+    cu_l[b + 1] = (int32_t)t;
+  }
+  return CPATTN_OK;
+}
+
+CPATTN_API cpattn_status cpattn_partition_hw(const cpattn_tensor* src_global, cpattn_tensor* dst_local,
+                                             const int32_t* cu_dev, int32_t nseq, int32_t frames, int32_t H,
+                                             int32_t W, int32_t split_h, int32_t split_w, int32_t rank,
+                                             void* stream) {
+  if (!hw_valid(frames, H, W, split_h, split_w)) return CPATTN_ERR_INVALID_ARG;
+  const int32_t hw[4] = {H, W, split_h, split_w};
+  return partition_common(src_global, dst_local, cu_dev, nseq, split_h * split_w, rank, stream, false, 0, 0, hw);
+}
+
+CPATTN_API cpattn_status cpattn_unpartition_hw(const cpattn_tensor* src_local, cpattn_tensor* dst_global,
+                                               const int32_t* cu_dev, int32_t nseq, int32_t frames, int32_t H,
+                                               int32_t W, int32_t split_h, int32_t split_w, int32_t rank,
+                                               void* stream) {
+  if (!hw_valid(frames, H, W, split_h, split_w)) return CPATTN_ERR_INVALID_ARG;
+  const int32_t hw[4] = {H, W, split_h, split_w};
+  return partition_common(src_local, dst_global, cu_dev, nseq, split_h * split_w, rank, stream, true, 0, 0, hw);
+}
+
 CPATTN_API int64_t cpattn_count_pairs(const int32_t* cu_g, int32_t nseq, cpattn_mask_mode mode,
                                       const cpattn_step* st) {
   if (!cu_g || nseq < 0 || check_step(st, mode) != CPATTN_OK || cu_g[0] != 0) return -1;
@@ -318,7 +392,7 @@ CPATTN_API int64_t cpattn_count_pairs(const int32_t* cu_g, int32_t nseq, cpattn_
   int64_t total = 0;
   for (int b = 0; b < nseq; ++b) {
     const int64_t L = (int64_t)cu_g[b + 1] - cu_g[b];
-    if (L < 0 || (cp > 1 && L % (2 * cp))) return -1;
+    if (L < 0 || (cp > 1 && L % (mode == CPATTN_MASK_BIDIR ? cp : 2 * cp))) return -1;
     if (mode == CPATTN_MASK_TF_BLOCK) {
       const int64_t B = st->tf_chunk_tokens, N = st->tf_num_chunks;
       if (L != 2 * B * N) return -1;
@@ -337,6 +411,10 @@ CPATTN_API int64_t cpattn_count_pairs(const int32_t* cu_g, int32_t nseq, cpattn_
     }
     if (cp == 1) {
       total += mode == CPATTN_MASK_BIDIR ? L * L : causal_block_pairs(0, L, 0, L);
+      continue;
+    }
+    if (mode == CPATTN_MASK_BIDIR) {    // any split: every local query sees every local key of the source
+      total += (L / cp) * (L / cp);
       continue;
     }
     const int64_t C = L / (2 * cp);

@@ -206,7 +206,8 @@ struct PartArgs {
   int row_bytes;                            // head_dim * element size (multiple of 16)
   int cp, rank;
   int scatter;                              // 0: global -> local, 1: local -> global
-  int tf_b, tf_n;                           // > 0: balanced teacher-forcing split, else zigzag
+  int tf_b, tf_n;                           // > 0: balanced teacher-forcing split
+  int hw_h, hw_w, hw_sh, hw_sw;             // > 0: height/width split of frames x H x W tokens
 };
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);

@@ -142,6 +142,9 @@ hipError_t launch_delta(const DeltaArgs& a, hipStream_t stream) {
 // 2cp-1-r).  Local row t of sequence b sits at local offset o = t - cu_l[b]
 // with cu_l[b] = cu_g[b]/cp; its global row is
 //   cu_g[b] + (o < C ? r*C + o : (2cp-1-r)*C + o - C),  C = L_b/(2cp).
+// Under the height/width split (LongCat-Video context-parallel page) local
+// row o of a frames x H x W sample is row o mod (th*tw) of frame o/(th*tw)
+// inside the rank's grid cell of th x tw tokens.
 // Under the balanced teacher-forcing split ("Scaling Video Training with
 // Parallelism", section 4) local row o of a sequence is, with m = N/cp time
 // chunks per rank, row o mod B of the rank's (o/B mod m)-th time chunk in the
@@ -174,7 +177,15 @@ __global__ __launch_bounds__(256) void partition_kernel(PartArgs a) {
     const int64_t gb = a.cu[lo];
     const int64_t len = (int64_t)a.cu[lo + 1] - gb;
     const int64_t o = t - gb / a.cp;
-    if (a.tf_b > 0) {
+    if (a.hw_h > 0) {
+      // height/width split: rank r's grid cell (r / sw, r mod sw) of every
+      // frame, cell rows top to bottom, each left to right
+      const int64_t th = a.hw_h / a.hw_sh, tw = a.hw_w / a.hw_sw, cell = th * tw;
+      const int64_t f = o / cell, rem = o - f * cell;
+      const int64_t hh = rem / tw, ww = rem - hh * tw;
+      const int64_t rh = a.rank / a.hw_sw, rw = a.rank - rh * a.hw_sw;
+      g = gb + (f * a.hw_h + rh * th + hh) * a.hw_w + rw * tw + ww;
+    } else if (a.tf_b > 0) {
       // balanced teacher forcing: [clean chunks of the rank ; noisy chunks],
       // N/cp time chunks of B rows in each stream
       const int64_t B = a.tf_b, m = a.tf_n / a.cp;
@@ -190,8 +201,8 @@ __global__ __launch_bounds__(256) void partition_kernel(PartArgs a) {
   if (g < 0 || g >= a.global_tokens) return;
   const int64_t ls = a.scatter ? t : g;   // source row
   const int64_t ld = a.scatter ? g : t;   // destination row
-  const u32x4 v = *(const u32x4*)(a.src + ls * a.src_st + h * a.src_sh + c * 16);
-  *(u32x4*)(a.dst + ld * a.dst_st + h * a.dst_sh + c * 16) = v;
+  const u32x4 v = ld_nt((const u32x4*)(a.src + ls * a.src_st + h * a.src_sh + c * 16));
+  st_nt(v, (u32x4*)(a.dst + ld * a.dst_st + h * a.dst_sh + c * 16));
 }
 
 hipError_t launch_partition(const PartArgs& a, hipStream_t stream) {

@@ -221,12 +221,14 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
                  (int64_t)p1 > a.tokens_p || (int64_t)s1 > a.tokens_s;
       const int lp = p1 - p0, ls = s1 - s0;
       const bool tfs = a.mask == CPATTN_MASK_TF_BLOCK && cp > 1;   // balanced teacher-forcing split
-      if (cp > 1) bad = bad || (lp & 1) || lp != ls;
+      // zigzag halves matter only where positions do; BIDIR takes any split
+      const bool halves = cp > 1 && a.mask != CPATTN_MASK_BIDIR;
+      if (cp > 1) bad = bad || (halves && (lp & 1)) || lp != ls;
       if (a.mask == CPATTN_MASK_TF_BLOCK) bad = bad || lp != ls || lp != 2 * a.tf_b * (a.tf_n / cp);
       if (bad) atomicOr(&s_err, 1);
       if (!bad) {
         if (tfs) cnt = 2 * (a.tf_n / cp) * ceil_div(a.tf_b, a.tile_p);
-        else if (cp > 1) cnt = 2 * ceil_div(lp >> 1, a.tile_p);
+        else if (halves) cnt = 2 * ceil_div(lp >> 1, a.tile_p);
         else cnt = ceil_div(lp, a.tile_p);
       }
     }
@@ -274,8 +276,9 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
       atomicAdd(&s_bins[min(it.cost, kBins - 1)], 1);
       continue;
     }
+    const bool halves = cp > 1 && a.mask != CPATTN_MASK_BIDIR;
     int chunk_off = 0, chunk_len = lp, t = t_in_seq;
-    if (cp > 1) {
+    if (halves) {
       const int half = lp >> 1, per = ceil_div(half, a.tile_p);
       const int hsel = t_in_seq >= per ? 1 : 0;
       t = t_in_seq - hsel * per;
@@ -288,9 +291,9 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
     it.seq = b;
     it.row0 = pr0 + off0;
     it.nrows = nrows;
-    it.pos0 = zigzag_pos(off0, lp, cp, a.rank_p);
+    it.pos0 = halves ? zigzag_pos(off0, lp, cp, a.rank_p) : off0;
     int cb[2], cpos[2], clen[2], nch;
-    if (cp > 1) {
+    if (halves) {
       const int half = ls >> 1;
       nch = 2;
       cb[0] = sr0;        cpos[0] = a.rank_s * half;                clen[0] = half;

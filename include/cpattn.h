@@ -178,6 +178,34 @@ cpattn_status cpattn_unpartition_tf(const cpattn_tensor* src_local, cpattn_tenso
                                     int32_t cp, int32_t rank, int32_t tf_chunk_tokens,
                                     int32_t tf_num_chunks, void* stream);
 
+/* ---- height/width token split ----------------------------------------------
+ * LongCat-Video context-parallel page (split_tensor_in_cp_2d,
+ * get_optimal_split): video latent tokens are split along height, then width,
+ * with the factors chosen automatically as the split closest to square.
+ * Readings taken (the page gives no formula): every sample is frames x H x W
+ * tokens in row-major order; cp = split_h * split_w with H % split_h == 0 and
+ * W % split_w == 0, choosing the split whose per-rank tile
+ * (H/split_h) x (W/split_w) is closest to square (ties: smaller split_h);
+ * rank r holds grid cell (r / split_w, r mod split_w) of every frame, frame
+ * by frame, cell rows top to bottom and each left to right.  Attention over
+ * such shares is order-free under CPATTN_MASK_BIDIR, which the ring steps
+ * accept at any cp (each local sequence is one block of rows).
+ * cpattn_split_hw returns the factors (CPATTN_ERR_INVALID_ARG when no even
+ * split exists); the index and gather/scatter functions follow the zigzag
+ * ones above with cp = split_h * split_w and every sequence frames*H*W long. */
+cpattn_status cpattn_split_hw(int32_t H, int32_t W, int32_t cp, int32_t* split_h, int32_t* split_w);
+cpattn_status cpattn_partition_index_hw(const int32_t* cu_seqlens_global_host, int32_t num_seqs, int32_t frames,
+                                        int32_t H, int32_t W, int32_t split_h, int32_t split_w, int32_t rank,
+                                        int32_t* cu_seqlens_local_host, int64_t* local_to_global_host);
+cpattn_status cpattn_partition_hw(const cpattn_tensor* src_global, cpattn_tensor* dst_local,
+                                  const int32_t* cu_seqlens_global_dev, int32_t num_seqs, int32_t frames,
+                                  int32_t H, int32_t W, int32_t split_h, int32_t split_w, int32_t rank,
+                                  void* stream);
+cpattn_status cpattn_unpartition_hw(const cpattn_tensor* src_local, cpattn_tensor* dst_global,
+                                    const int32_t* cu_seqlens_global_dev, int32_t num_seqs, int32_t frames,
+                                    int32_t H, int32_t W, int32_t split_h, int32_t split_w, int32_t rank,
+                                    void* stream);
+
 /* ---- Ulysses sequence <-> head exchange ------------------------------------
  * "Scaling Video Training with Parallelism", SP landscape (DeepSpeed-Ulysses;
  * USP / LoongTrain 2D-Attention): Ulysses shards the sequence and exchanges
@@ -229,7 +257,8 @@ cpattn_status cpattn_workspace_status(const void* workspace, void* stream, cpatt
  *   k, v         [Tk, Hkv, d]     K/V share of rank (rank - step) mod cp
  *   cu_seqlens_q_dev, cu_seqlens_k_dev  local int32[num_seqs+1]; for cp > 1
  *                and for CAUSAL / TF_BLOCK the per-sequence lengths of q and k
- *                must match (every rank's share has the same lengths).
+ *                must match (every rank's share has the same lengths); for
+ *                CAUSAL at cp > 1 they are even (two zigzag chunks).
  *   out_partial  [Tq, Hq, d]      same dtype as q; every row of every sequence
  *                                 is overwritten (0 for rows with no key)
  *   lse_partial_dev  fp32 [Hq][Tq]  (-inf for rows with no key)

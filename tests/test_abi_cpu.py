@@ -207,3 +207,34 @@ def test_ulysses_exchange_rejects_bad_input():
     assert _s2h(sh[:3], 0, _FakeTensor((100, 2, 128), bf, ptr=0x900000)) == c.ERR_INVALID_ARG  # too few rows
     assert _s2h(sh[:3], 0, _FakeTensor((192, 2, 64), bf, ptr=0x900000)) == c.ERR_INVALID_ARG   # head_dim differs
     assert _s2h([], 0, dst) == c.ERR_INVALID_ARG                           # no shards
+
+
+@pytest.mark.parametrize("H,W,cp", [(60, 104, 8), (64, 64, 8), (48, 48, 6), (12, 20, 4), (30, 32, 8), (7, 14, 2),
+                                    (90, 160, 16), (5, 5, 1)])
+def test_split_hw_matches_oracle(H, W, cp):
+    assert c.cpattn_split_hw(H, W, cp) == oracle.hw_split.optimal_split(H, W, cp)
+
+
+def test_split_hw_rejects_uneven():
+    with pytest.raises(c.CpattnError):
+        c.cpattn_split_hw(30, 30, 8)
+
+
+@pytest.mark.parametrize("frames,H,W,cp,nseq", [(2, 4, 6, 4, 1), (3, 6, 4, 6, 2), (31, 30, 52, 8, 1), (1, 8, 8, 8, 2)])
+def test_partition_index_hw_matches_oracle(frames, H, W, cp, nseq):
+    split = c.cpattn_split_hw(H, W, cp)
+    cu = np.arange(nseq + 1, dtype=np.int32) * (frames * H * W)
+    for r in range(cp):
+        cu_l, l2g = c.cpattn_partition_index_hw(cu, frames, H, W, split, r)
+        cu_o, l2g_o, _, _ = oracle.hw_split.local_rows(cu, frames, H, W, split, r)
+        assert np.array_equal(cu_l, cu_o)
+        assert np.array_equal(l2g, l2g_o)
+
+
+def test_count_pairs_bidir_any_split():
+    """BIDIR at cp > 1 counts (L/cp)^2 per sequence and step for any split,
+    also when L/cp is odd."""
+    L = 31 * 30 * 52
+    cu = np.array([0, L], np.int32)
+    for s in range(8):
+        assert c.cpattn_count_pairs(cu, oracle.BIDIR, c.make_step(8, 3, s)) == (L // 8) ** 2
