@@ -405,7 +405,7 @@ def main():
     tflops = (fwd_flops + bwd_flops) / (wall_ms * 1e-3) / 1e12
 
     # dominant kernel and its roofline
-    kern = {"fwd_step": ("cpattn::fwd_bf16_kernel<128, 4, 1>", fwd_flops / w.cp),
+    kern = {"fwd_step": ("cpattn::fwd_bf16_kernel<128, 4>", fwd_flops / w.cp),
             "bwd_step": ("cpattn::(anonymous namespace)::bwd_bf16_kernel<128>", bwd_flops / w.cp)}
     dom = max((k for k in kern if k in st), key=lambda k: st[k]["total_ms"])
     kname, flops_per_launch = kern[dom]

@@ -5,12 +5,7 @@
 //
 // bf16 path (gfx950 MFMA).  One workgroup = one tile of 128 query rows x one
 // q-head; 4 waves of 32 query rows each, compiled for two waves per SIMD
-// (two workgroups per CU, 64 KiB of LDS each), so that one wave's softmax
-// runs while the other's MFMAs do (with one wave per SIMD the MFMA drains,
-// cross-lane exchanges and barriers stall the SIMD).  The kernel is also
-// templated for 64 query rows per wave (two MFMA column blocks sharing every
-// K operand read); that form needs one wave per SIMD and measured slower.
-// Per key tile of 64 rows:
+// (two workgroups per CU, 64 KiB of LDS each).  Per key tile of 64 rows:
 //   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K from LDS, Q in registers;
 //                    the transposed product puts one query per lane column,
 //                    so row statistics are in-lane plus one lane^32 swap.
@@ -20,11 +15,14 @@
 //   O^T += V^T P^T   P rounded to bf16 straight from the accumulator
 //                    registers; V^T operands come from the row-major V tile
 //                    through transposing LDS reads (ds_read_b64_tr_b16).
-// K and V tiles move global -> LDS with direct loads (no register staging),
-// double-buffered with one barrier per tile; the next tile's loads are in
-// flight during the current tile's math.  Workgroups are mapped so that the
-// q-heads of one GQA group and the tiles of one kv-head land on the same XCD,
-// keeping their K/V in that XCD's L2.
+// The tile loop is software-pipelined across tiles: the S^T products of
+// tile j + 1 and the PV products of tile j carry tile j's softmax and tile
+// j + 1's row max (see the kernel).  K and V tiles move global -> LDS with
+// direct loads (no register staging), double-buffered with one barrier per
+// tile.  Workgroups are mapped so that the q-heads of one GQA group and the
+// tiles of one kv-head land on the same XCD, keeping their K/V in that
+// XCD's L2.  Measured alternatives: 64 query rows per wave (one wave per
+// SIMD) and per-32-key softmax blocks were slower.
 //
 // fp32 path: a plain per-row kernel (one query row per thread, exact expf)
 // for fp32 inputs; it exists for accuracy checks, not speed.
@@ -44,20 +42,31 @@ constexpr float kRescale = 8.0f;
 #ifndef CPATTN_FWD_PF
 #define CPATTN_FWD_PF 3
 #endif
-constexpr int kFwdPF = CPATTN_FWD_PF;   // K operand reads ahead of their products
+constexpr int kFwdPF = CPATTN_FWD_PF;   // operand reads ahead of their products
 
 
 
-// Waves per SIMD the kernel is compiled for: two when each wave owns 32
-// queries (so one wave's softmax overlaps the other's MFMAs), else one.
-template <int QB>
-struct FwdOcc { static constexpr int value = QB == 1 ? 2 : 1; };
-
-template <int D, int NW, int QB>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FwdOcc<QB>::value, FwdOcc<QB>::value)))
+// ---------------------------------------------------------------------------
+// bf16 kernel, software-pipelined across key tiles (32 queries per wave,
+// two waves per SIMD).  Iteration j issues the S^T products of tile j + 1 and the PV
+// products of tile j, and spreads tile j's softmax over them:
+//   S^T(j+1) products:  rescale decision of tile j, exp + pack of its key
+//                       block 0, then exp of key block 1
+//   PV(j) products:     rest of block 1's exp and its pack (before the block-1
+//                       products need it), then mask and row max of tile j + 1
+// K of tile j + 2 and V of tile j + 1 load during iteration j into the
+// buffers that tiles j and j - 1 released, so one barrier per iteration and
+// double buffering suffice.  Operand reads run PF products ahead; every
+// product slot is fenced so the interleave holds.
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(FwdArgs a) {
   constexpr int BN = 64;
-  constexpr int QW = 32 * QB;                 // query rows per wave
+  constexpr int NK = D / 16;       // k-steps of one 32-key S^T block; PV products per 16-key k-step pair
+  constexpr int NS = 2 * NK;       // S^T products per tile (two key blocks)
+  constexpr int NP = 4 * (D / 32); // PV products per tile
+  constexpr int PF = kFwdPF;
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][BN * D];
 
@@ -68,8 +77,7 @@ void fwd_bf16_kernel(FwdArgs a) {
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int col = lane & 31, hh = lane >> 5;
-
-  const int64_t kst = a.k_st * 2, vst = a.v_st * 2;     // row strides in bytes
+  const int64_t kst = a.k_st * 2, vst = a.v_st * 2;
   const char* kbase = (const char*)a.k + (int64_t)g * a.k_sh * 2;
   const char* vbase = (const char*)a.v + (int64_t)g * a.v_sh * 2;
   TileLoader<D, BN, NW> lk, lv;
@@ -79,183 +87,225 @@ void fwd_bf16_kernel(FwdArgs a) {
   const int nt0 = it.nseg > 0 ? ceil_div(it.seg[0].n, BN) : 0;
   const int nt1 = it.nseg > 1 ? ceil_div(it.seg[1].n, BN) : 0;
   const int ntiles = nt0 + nt1;
-  auto issue = [&](int j, int buf) {
+  auto tile_at = [&](int j, int& t0, Segment& sg) {
     const int s = j < nt0 ? 0 : 1;
-    const int t0 = (j - (s ? nt0 : 0)) * BN;
-    const Segment& sg = it.seg[s];
-    const int nvalid = min(BN, sg.n - t0);
-    const int64_t row = sg.row + t0;
-    lk.issue(s_k[buf], kbase + row * kst, nvalid, kst);
-    lv.issue(s_v[buf], vbase + row * vst, nvalid, vst);
+    t0 = (j - (s ? nt0 : 0)) * BN;
+    sg = it.seg[s];
   };
-  if (ntiles > 0) issue(0, 0);
+  auto issue_k = [&](int j) {
+    int t0;
+    Segment sg;
+    tile_at(j, t0, sg);
+    lk.issue(s_k[j & 1], kbase + (int64_t)(sg.row + t0) * kst, min(BN, sg.n - t0), kst);
+  };
+  auto issue_v = [&](int j) {
+    int t0;
+    Segment sg;
+    tile_at(j, t0, sg);
+    lv.issue(s_v[j & 1], vbase + (int64_t)(sg.row + t0) * vst, min(BN, sg.n - t0), vst);
+  };
+  if (ntiles > 0) {
+    issue_k(0);
+    issue_v(0);
+    if (ntiles > 1) issue_k(1);
+  }
 
-  // Q operand (B of S^T = K Q^T): lane holds Q[row][16*ks + 8*hh + 0..7]
-  bf16x8 qreg[QB][D / 16];
-  KeyRanges kr[QB];
-  bool row_ok[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int r = wave * QW + qb * 32 + col;
-    row_ok[qb] = r < it.nrows;
-    kr[qb] = key_ranges(a.mask, it.pos0 + r, a.tf_b, a.tf_n);
+  const int r = wave * 32 + col;
+  const bool row_ok = r < it.nrows;
+  const KeyRanges kr = key_ranges(a.mask, it.pos0 + r, a.tf_b, a.tf_n);
+  bf16x8 qreg[NK];
+  {
     const uint16_t* src = (const uint16_t*)a.q + (int64_t)(it.row0 + r) * a.q_st + (int64_t)h * a.q_sh + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = 0; ks < NK; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (row_ok[qb]) raw = *(const u32x4*)(src + 16 * ks);
-      qreg[qb][ks] = __builtin_bit_cast(bf16x8, raw);
+      if (row_ok) raw = *(const u32x4*)(src + 16 * ks);
+      qreg[ks] = __builtin_bit_cast(bf16x8, raw);
     }
   }
+  f32x16 acc_o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
-  f32x16 acc_o[QB][D / 32];
-  float m_run[QB], l_run[QB];
+  // S^T of one tile: two 32-key accumulator chains, key block 0 first.
+  f32x16 sacc[2][2];     // [tile parity][key block]
+  float smax[2];         // scaled row max of the tile held in sacc[parity]
+  // mask of a partial tile, then its scaled row max
+  auto mask_block = [&](f32x16 (&st)[2], int kb, int t0, const Segment& sg) {
+    const int kbase0 = t0 + 32 * kb + 4 * hh;
+    const int rem = sg.n - kbase0;
+    const int pbase = sg.pos + kbase0;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      const int off = 8 * (i >> 2) + (i & 3);
+      st[kb][i] = ((off < rem) & in_ranges(kr, pbase + off)) ? st[kb][i] : -INFINITY;
+    }
+  };
+  auto rowmax_part = [&](const f32x16& v, float m) {
+    m = max3f(m, v[0], v[1]);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc_o[qb][db][i] = 0.f;
-  }
+    for (int i = 2; i + 1 < 16; i += 2) m = max3f(m, v[i], v[i + 1]);
+    return fmaxf(m, v[15]);
+  };
 
-  // One key tile; BUF is a compile-time buffer index so every LDS offset is
-  // an immediate.
-  auto tile = [&](int j, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    wait_loads();
+  // prologue: S^T of tile 0 with its mask and row max
+  if (ntiles > 0) {
+    wait_vmcnt_tiles<TileLoader<D, BN, NW>::PER>(ntiles > 1 ? 2 : 1);   // K(0) in; V(0), K(1) may load
     __syncthreads();
-    if (j + 1 < ntiles) issue(j + 1, buf ^ 1);
-    const int s = j < nt0 ? 0 : 1;
-    const int t0 = (j - (s ? nt0 : 0)) * BN;
-    const Segment sg = it.seg[s];
-    const uint16_t* tk = s_k[buf];
-    const uint16_t* tv = s_v[buf];
-    const bool full = t0 >= sg.full_lo && t0 + BN <= sg.full_hi;
-    // S^T for the whole 64-key tile, then one softmax update, then PV. The
-    // two 32-key blocks of S^T run as one accumulator chain each, block 0
-    // first, so block 0's mask and partial row max are done under block 1's
-    // products. K operands are read PF products ahead; each step is fenced.
-    static_assert(QB == 1 && BN == 64, "the tile schedule covers one 32-query block and two key blocks");
-    constexpr int NK = D / 16;
-    f32x16 acc_s[QB][BN / 32];
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc_s[0][kb][i] = 0.f;
-    auto mask_block = [&](int kb) {
-      if (!full) {
-        const int kbase0 = t0 + kb * 32 + 4 * hh;     // key offset of register 0
-        const int rem = sg.n - kbase0;                 // registers at offset >= rem are past the segment
-        const int pbase = sg.pos + kbase0;
+      for (int i = 0; i < 16; ++i) sacc[0][kb][i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int off = 8 * (i >> 2) + (i & 3);
-          acc_s[0][kb][i] = ((off < rem) & in_ranges(kr[0], pbase + off)) ? acc_s[0][kb][i] : -INFINITY;
-        }
-      }
-    };
-    bf16x8 kop[2 * NK];
-    auto read_k = [&](int u) { kop[u] = read_row8<D>(tk, 32 * (u / NK), col, u % NK, hh); };
-#pragma unroll
-    for (int u = 0; u < kFwdPF; ++u) read_k(u);
-    float mx0 = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2 * NK; ++u) {
-      if (u + kFwdPF < 2 * NK) read_k(u + kFwdPF);
-      acc_s[0][u / NK] = mfma32(kop[u], qreg[0][u % NK], acc_s[0][u / NK]);
-      if (u == NK + 2) mask_block(0);
-      if (u == NK + 3)
-        mx0 = max3f(max3f(max3f(max3f(acc_s[0][0][0], acc_s[0][0][1], acc_s[0][0][2]), acc_s[0][0][3], acc_s[0][0][4]),
-                          acc_s[0][0][5], acc_s[0][0][6]), acc_s[0][0][7], acc_s[0][0][8]);
-      if (u == NK + 4)
-        mx0 = fmaxf(max3f(max3f(max3f(mx0, acc_s[0][0][9], acc_s[0][0][10]), acc_s[0][0][11], acc_s[0][0][12]),
-                          acc_s[0][0][13], acc_s[0][0][14]), acc_s[0][0][15]);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int u = 0; u < NS; ++u)
+      sacc[0][u / NK] = mfma32(read_row8<D>(s_k[0], 32 * (u / NK), col, u % NK, hh), qreg[u % NK], sacc[0][u / NK]);
+    int t0;
+    Segment sg;
+    tile_at(0, t0, sg);
+    if (!(t0 >= sg.full_lo && t0 + BN <= sg.full_hi)) {
+      mask_block(sacc[0], 0, t0, sg);
+      mask_block(sacc[0], 1, t0, sg);
     }
-    if (NK + 2 >= 2 * NK) mask_block(0);   // D = 64: block 1 is too short to carry them
-    if (NK + 3 >= 2 * NK)
-      mx0 = max3f(max3f(max3f(max3f(acc_s[0][0][0], acc_s[0][0][1], acc_s[0][0][2]), acc_s[0][0][3], acc_s[0][0][4]),
-                        acc_s[0][0][5], acc_s[0][0][6]), acc_s[0][0][7], acc_s[0][0][8]);
-    if (NK + 4 >= 2 * NK)
-      mx0 = fmaxf(max3f(max3f(max3f(mx0, acc_s[0][0][9], acc_s[0][0][10]), acc_s[0][0][11], acc_s[0][0][12]),
-                        acc_s[0][0][13], acc_s[0][0][14]), acc_s[0][0][15]);
-    mask_block(1);
-    float mt[QB];
-    bool need = false;
-    {
-      float mx = mx0;
-#pragma unroll
-      for (int i = 0; i + 1 < 16; i += 2) mx = max3f(mx, acc_s[0][1][i], acc_s[0][1][i + 1]);
-      mt[0] = max_halves(mx) * a.scale_log2;
-      need |= mt[0] > m_run[0] + kRescale;
-    }
-    if (__any(need)) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float m_new = fmaxf(m_run[qb], mt[qb]);
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
+    smax[0] = max_halves(rowmax_part(sacc[0][1], rowmax_part(sacc[0][0], -INFINITY))) * a.scale_log2;
+  }
+
+  // MORE: a tile j + 1 follows (compile-time, so the product slots carry no
+  // branches on it)
+  auto iter = [&](int j, auto parc, auto morec) {
+    constexpr int P = decltype(parc)::value;       // j & 1: V(j) buffer, sacc/smax slot of tile j
+    constexpr int Q = P ^ 1;                       // slot of tile j + 1
+    constexpr bool more = decltype(morec)::value;
+    wait_loads();                                  // K(j+1), V(j) in (issued an iteration ago)
+    __syncthreads();
+    if (j + 2 < ntiles) issue_k(j + 2);            // into K(j)'s buffer
+    if (more) issue_v(j + 1);                      // into V(j-1)'s buffer
+    const uint16_t* tk = s_k[Q];
+    const uint16_t* tv = s_v[P];
+    int t1 = 0;
+    Segment sg1 = it.seg[0];
+    if (more) tile_at(j + 1, t1, sg1);
+    const bool full1 = t1 >= sg1.full_lo && t1 + BN <= sg1.full_hi;
+
+    // ---- softmax of tile j, in slots -------------------------------------
+    bf16x8 pb[4];
+    float m_use = 0.f;
+    auto rescale = [&]() {
+      const float mt = smax[P];
+      if (__any(mt > m_run + kRescale)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc_o[qb][db][i] *= alpha;
+          for (int i = 0; i < 16; ++i) acc_o[db][i] *= alpha;
       }
+      m_use = m_run == -INFINITY ? 0.f : m_run;
+    };
+    auto exps = [&](int kb, int i0, int i1) {
+#pragma unroll
+      for (int i = i0; i < i1; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sacc[P][kb][i] * a.scale_log2 - m_use);
+        sacc[P][kb][i] = p;
+        l_run += p;
+      }
+    };
+    auto pack = [&](int kb) {
+      pb[2 * kb] = pack_b(sacc[P][kb], 0);
+      pb[2 * kb + 1] = pack_b(sacc[P][kb], 1);
+      asm volatile("" : "+v"(pb[2 * kb]), "+v"(pb[2 * kb + 1]));
+    };
+    float mx1 = -INFINITY;
+    // work of slot `sl` (0 .. NS + NP - 1): S^T(j+1) products come first
+    // Slot s carries its work after its product.  Block 0's pack lands in the
+    // S^T slots (before PV product 0); block 1's before PV product NP/2,
+    // the first one that reads it.
+    constexpr int EA = NS / 2 - 1;                 // slots 1..EA: block-0 exps; EA+1: its pack
+    constexpr int B0 = EA + 2, B1 = NS + NP / 2 - 2;   // [B0, B1): block-1 exps; B1: its pack
+    static_assert(EA + 1 < NS && B1 < NS + NP / 2 && B1 > B0, "packs precede their PV products");
+    auto slot_work = [&](int sl) {
+      if (sl == 0) rescale();
+      if (sl >= 1 && sl <= EA) exps(0, (sl - 1) * 16 / EA, sl * 16 / EA);
+      if (sl == EA + 1) pack(0);
+      if (sl >= B0 && sl < B1) exps(1, (sl - B0) * 16 / (B1 - B0), (sl - B0 + 1) * 16 / (B1 - B0));
+      if (sl == B1) pack(1);
+      if (more) {
+        if (sl == NS + NP / 2 && !full1) { mask_block(sacc[Q], 0, t1, sg1); mask_block(sacc[Q], 1, t1, sg1); }
+        if (sl == NS + NP / 2 + 1) mx1 = rowmax_part(sacc[Q][0], -INFINITY);
+        if (sl == NS + NP / 2 + 2) smax[Q] = max_halves(rowmax_part(sacc[Q][1], mx1)) * a.scale_log2;
+      }
+    };
+
+    // ---- products ----------------------------------------------------------
+    bf16x8 kop[NS], vop[NP];
+    auto read_k = [&](int u) { kop[u] = read_row8<D>(tk, 32 * (u / NK), col, u % NK, hh); };
+    auto read_v = [&](int m) {          // PV product m: k-step pair ps = m / (D/32), d-block m % (D/32)
+      vop[m] = read_tr<D>(tv, 16 * (m / (D / 32)), 32 * (m % (D / 32)), lane);
+    };
+    auto read_op = [&](int x) {         // operand x of the iteration's product sequence
+      if (x < NS) { if (more) read_k(x); }
+      else read_v(x - NS);
+    };
+    if (more) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[Q][kb][i] = 0.f;
     }
-    bf16x8 pb[QB][BN / 16];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+    for (int x = 0; x < PF; ++x) read_op(more ? x : NS + x);
 #pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(acc_s[qb][kb][i] * a.scale_log2 - m_use);
-          acc_s[qb][kb][i] = p;
-          l_run[qb] += p;
-        }
-        pb[qb][2 * kb] = pack_b(acc_s[qb][kb], 0);
-        pb[qb][2 * kb + 1] = pack_b(acc_s[qb][kb], 1);
+    for (int u = 0; u < NS; ++u) {
+      if (more) {
+        if (u + PF < NS + NP) read_op(u + PF);
+        sacc[Q][u / NK] = mfma32(kop[u], qreg[u % NK], sacc[Q][u / NK]);
       }
+      slot_work(u);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // consecutive MFMAs go to different accumulators (independent chains)
 #pragma unroll
-    for (int ps = 0; ps < BN / 16; ++ps)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 av = read_tr<D>(tv, 16 * ps, 32 * db, lane);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc_o[qb][db] = mfma32(av, pb[qb][ps], acc_o[qb][db]);
-      }
+    for (int m = 0; m < NP; ++m) {
+      if (m + PF < NP) read_v(m + PF);
+      acc_o[m % (D / 32)] = mfma32(vop[m], pb[m / (D / 32)], acc_o[m % (D / 32)]);
+      slot_work(NS + m);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  for (int j = 0; j < ntiles; j += 2) {
-    tile(j, std::integral_constant<int, 0>{});
-    if (j + 1 < ntiles) tile(j + 1, std::integral_constant<int, 1>{});
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using T = std::true_type;
+  using F = std::false_type;
+  int j = 0;
+  for (; j + 2 < ntiles; j += 2) {
+    iter(j, I0{}, T{});
+    iter(j + 1, I1{}, T{});
+  }
+  if (j + 1 < ntiles) {
+    iter(j, I0{}, T{});
+    iter(j + 1, I1{}, F{});
+  } else if (j < ntiles) {
+    iter(j, I0{}, F{});
   }
 
-  // ---- epilogue ----
+  const float l = sum_halves(l_run);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (!row_ok) return;
+  uint16_t* op = (uint16_t*)a.out + (int64_t)(it.row0 + r) * a.o_st + (int64_t)h * a.o_sh;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l = sum_halves(l_run[qb]);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    if (!row_ok[qb]) continue;
-    const int r = wave * QW + qb * 32 + col;
-    uint16_t* op = (uint16_t*)a.out + (int64_t)(it.row0 + r) * a.o_st + (int64_t)h * a.o_sh;
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int i4 = 0; i4 < 4; ++i4) {
+      bf16x4 w;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc_o[qb][db][4 * i4 + e] * inv);
-        *(u32x2*)(op + db * 32 + 8 * i4 + 4 * hh) = __builtin_bit_cast(u32x2, w);
-      }
-    if (hh == 0)
-      a.lse[(int64_t)h * a.tq + it.row0 + r] =
-          l > 0.f ? (m_run[qb] + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
-  }
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc_o[db][4 * i4 + e] * inv);
+      *(u32x2*)(op + db * 32 + 8 * i4 + 4 * hh) = __builtin_bit_cast(u32x2, w);
+    }
+  if (hh == 0)
+    a.lse[(int64_t)h * a.tq + it.row0 + r] = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -304,23 +354,19 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
   a.lse[(int64_t)h * a.tq + it.row0 + r] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
-#ifndef CPATTN_FWD_QB
-#define CPATTN_FWD_QB 1
-#endif
-
 #ifndef CPATTN_FWD_WAVES
 #define CPATTN_FWD_WAVES 4
 #endif
-constexpr int kFwdWaves = CPATTN_FWD_WAVES, kFwdQB = CPATTN_FWD_QB;
-constexpr int kFwdTile = 32 * kFwdQB * kFwdWaves;
+constexpr int kFwdWaves = CPATTN_FWD_WAVES;
+constexpr int kFwdTile = 32 * kFwdWaves;   // query rows per workgroup
 
 int fwd_tile_rows(bool bf16) { return bf16 ? kFwdTile : 64; }
 
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream) {
   const dim3 grid(unit_grid(max_items, a.hkv, a.grp));
   if (bf16) {
-    if (d == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdWaves, kFwdQB>), grid, dim3(64 * kFwdWaves), 0, stream, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdWaves, kFwdQB>), grid, dim3(64 * kFwdWaves), 0, stream, a);
+    if (d == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdWaves>), grid, dim3(64 * kFwdWaves), 0, stream, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdWaves>), grid, dim3(64 * kFwdWaves), 0, stream, a);
   } else {
     if (d == 128) hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(64), 0, stream, a);
     else hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(64), 0, stream, a);

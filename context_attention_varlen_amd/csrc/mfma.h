@@ -127,6 +127,16 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// wait until at most `tiles` tile loads of PER instructions each are
+// outstanding (0..3), issue order being the order they are needed in
+template <int PER>
+__device__ __forceinline__ void wait_vmcnt_tiles(int tiles) {
+  if (tiles >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
+  else if (tiles == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
+  else if (tiles == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // 16-byte row read: the A (or B) operand slot of k-step ks for tile row
 // rc + rl (rc a multiple of 16), i.e. chunk 2*ks + hh of that row.
 typedef __attribute__((address_space(3))) const uint16_t lds_u16;
