@@ -22,7 +22,9 @@ What it follows (page titles as given at the top of each page):
     assignment (the chunk rule itself is not printed; see zigzag.py).
   * "Speeding up Variable-Length Training with Dynamic Context Parallelism and
     NVIDIA Megatron Core", section A2: packed THD layout with cu_seqlens and
-    FLOPs counted from real sequence lengths.
+    FLOPs counted from real sequence lengths; same section (Eq. 1-3 and the
+    three-stage heuristic) and section A7 (grid search near the knee of the
+    budget curve): the Dynamic-CP microbatch planner (dynamic_cp.py).
 
 Pins (what each function is checked against, other than itself) live in
 tests/test_oracle_*.py.  Every function here is pinned; none is marked
@@ -33,4 +35,4 @@ from .zigzag import (rank_chunks, local_rows, partition, count_pairs,  # noqa: F
                      step_source)
 from .softmax_attention import attention, attention_backward, bwd_delta, default_scale  # noqa: F401
 from .lse_merge import merge  # noqa: F401
-from . import hw_split, tf_split, ulysses  # noqa: F401
+from . import dynamic_cp, hw_split, tf_split, ulysses  # noqa: F401
