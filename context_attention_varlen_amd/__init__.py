@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libcpattn.so")
 
 CAUSAL, BIDIR, TF_BLOCK = 0, 1, 2
 F32, BF16 = 0, 1
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_INFEASIBLE = 0, 1, 2, 3, 4, 5
 
 EXPORTS = (
     "cpattn_version", "cpattn_status_string", "cpattn_last_hip_error", "cpattn_partition_index", "cpattn_partition",
@@ -31,6 +31,7 @@ EXPORTS = (
     "cpattn_partition_hw", "cpattn_unpartition_hw",
     "cpattn_count_pairs", "cpattn_workspace_size", "cpattn_workspace_status",
     "cpattn_fwd_step", "cpattn_merge", "cpattn_bwd_preprocess", "cpattn_bwd_step",
+    "cpattn_dcp_plan_batch", "cpattn_dcp_quotas",
 )
 
 
@@ -47,6 +48,22 @@ class Tensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int), ("tokens", ctypes.c_int64),
                 ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("stride_token", ctypes.c_int64), ("stride_head", ctypes.c_int64)]
+
+
+class DcpConfig(ctypes.Structure):
+    _fields_ = [("gpus", ctypes.c_int32), ("max_cp", ctypes.c_int32), ("pp", ctypes.c_int32),
+                ("vpp", ctypes.c_int32), ("mem_tokens", ctypes.c_int64), ("work_quad", ctypes.c_int64),
+                ("work_lin", ctypes.c_int64), ("m_min", ctypes.c_int32), ("m_max", ctypes.c_int32),
+                ("knee_radius", ctypes.c_int32)]
+
+
+class DcpPlan(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int32), ("knee", ctypes.c_int32), ("num_buckets", ctypes.c_int32),
+                ("step_time", ctypes.c_double), ("sample_bucket", ctypes.c_void_p),
+                ("bucket_cp", ctypes.c_void_p), ("bucket_slot", ctypes.c_void_p),
+                ("bucket_rank", ctypes.c_void_p), ("bucket_tokens", ctypes.c_void_p),
+                ("bucket_load", ctypes.c_void_p), ("times", ctypes.c_void_p), ("budget", ctypes.c_void_p),
+                ("bucket_capacity", ctypes.c_int32)]
 
 
 class Step(ctypes.Structure):
@@ -90,6 +107,8 @@ def _load():
         "cpattn_bwd_preprocess": (ctypes.c_int, [P, TP, P, P]),
         "cpattn_bwd_step": (ctypes.c_int, [TP, TP, TP, TP, P, P, P, P, I32, ctypes.c_int, SP, F,
                                            P, P, P, P, S, P]),
+        "cpattn_dcp_plan_batch": (ctypes.c_int, [P, I32, ctypes.POINTER(DcpConfig), ctypes.POINTER(DcpPlan)]),
+        "cpattn_dcp_quotas": (ctypes.c_int, [P, I32, I32, I32, ctypes.c_double, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -305,3 +324,41 @@ def cpattn_bwd_step(q, k, v, dout, lse, delta, cu_seqlens_q_dev, cu_seqlens_k_de
                               float(softmax_scale), _ptr(dq_accum), _ptr(dk_accum), _ptr(dv_accum),
                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "cpattn_bwd_step")
+
+
+# ---------------------------------------------------------------------------
+# Dynamic-CP planner (host only)
+# ---------------------------------------------------------------------------
+def cpattn_dcp_quotas(m, vpp, pp, total):
+    """Eq. 1-3 per-microbatch workload quotas of ranks running m[i] microbatches."""
+    mm = np.ascontiguousarray(m, dtype=np.int32)
+    W = np.zeros(len(mm), np.float64)
+    _check(_lib.cpattn_dcp_quotas(mm.ctypes.data, len(mm), vpp, pp, float(total), W.ctypes.data),
+           "cpattn_dcp_quotas")
+    return W
+
+
+def cpattn_dcp_plan_batch(lengths, gpus, max_cp, pp, vpp, mem_tokens, work_quad, work_lin, m_min, m_max,
+                          knee_radius=-1):
+    """Dynamic-CP plan of a global batch.  Returns a dict with m, knee,
+    step_time, sample_bucket [n] and the per-microbatch arrays cp, slot, rank,
+    tokens, load (length num_buckets), plus times and budget per m."""
+    L = np.ascontiguousarray(lengths, dtype=np.int32)
+    cap = int(gpus) * int(m_max)
+    nm = int(m_max) - int(m_min) + 1
+    arr = {"sample_bucket": np.zeros(len(L), np.int32), "cp": np.zeros(cap, np.int32),
+           "slot": np.zeros(cap, np.int32), "rank": np.zeros(cap, np.int32), "tokens": np.zeros(cap, np.int64),
+           "load": np.zeros(cap, np.float64), "times": np.zeros(max(nm, 0), np.float64),
+           "budget": np.zeros(max(nm, 0), np.float64)}
+    cfg = DcpConfig(gpus, max_cp, pp, vpp, mem_tokens, work_quad, work_lin, m_min, m_max, knee_radius)
+    out = DcpPlan(0, 0, 0, 0.0, arr["sample_bucket"].ctypes.data, arr["cp"].ctypes.data, arr["slot"].ctypes.data,
+                  arr["rank"].ctypes.data, arr["tokens"].ctypes.data, arr["load"].ctypes.data,
+                  arr["times"].ctypes.data, arr["budget"].ctypes.data, cap)
+    _check(_lib.cpattn_dcp_plan_batch(L.ctypes.data, len(L), ctypes.byref(cfg), ctypes.byref(out)),
+           "cpattn_dcp_plan_batch")
+    nb = out.num_buckets
+    res = {"m": out.m, "knee": out.knee, "num_buckets": nb, "step_time": out.step_time,
+           "sample_bucket": arr["sample_bucket"], "times": arr["times"], "budget": arr["budget"]}
+    for k in ("cp", "slot", "rank", "tokens", "load"):
+        res[k] = arr[k][:nb].copy()
+    return res

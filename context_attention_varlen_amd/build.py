@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcpattn.so")
-SOURCES = ["api.hip", "sched.hip", "fwd.hip", "bwd.hip", "elementwise.hip"]
+SOURCES = ["api.hip", "sched.hip", "fwd.hip", "bwd.hip", "elementwise.hip", "dcp_plan.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -136,6 +136,7 @@ CPATTN_API const char* cpattn_status_string(cpattn_status s) {
     case CPATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case CPATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case CPATTN_ERR_HIP: return "HIP runtime error";
+    case CPATTN_ERR_INFEASIBLE: return "no feasible plan";
   }
   return "unknown status";
 }

@@ -72,7 +72,8 @@ typedef enum {
     CPATTN_ERR_INVALID_ARG = 1,   /* bad pointer, size, stride, rank/step, cu_seqlens */
     CPATTN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (dtype, head_dim) */
     CPATTN_ERR_WORKSPACE = 3,     /* workspace missing or too small */
-    CPATTN_ERR_HIP = 4            /* a HIP runtime call or launch failed */
+    CPATTN_ERR_HIP = 4,           /* a HIP runtime call or launch failed */
+    CPATTN_ERR_INFEASIBLE = 5     /* planner: no plan fits the memory cap */
 } cpattn_status;
 
 typedef enum { CPATTN_F32 = 0, CPATTN_BF16 = 1 } cpattn_dtype;
@@ -305,6 +306,85 @@ cpattn_status cpattn_bwd_step(const cpattn_tensor* q, const cpattn_tensor* k, co
                               float softmax_scale, float* dq_accum_dev, float* dk_accum_dev,
                               float* dv_accum_dev, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* ---- Dynamic-CP microbatch planner (host only) -----------------------------
+ * "Speeding up Variable-Length Training with Dynamic Context Parallelism and
+ * NVIDIA Megatron Core", section A2 (data scheduling model, Eq. 1-3) and
+ * section A7 (zero-overhead runtime, Fig. 7): pack a global batch of
+ * variable-length samples into microbatches and give each microbatch its
+ * own power-of-two context-parallel size, so that short samples are not
+ * split and every rank gets the same modelled work.  The page describes the
+ * steps in words; the readings (constants, order, tie-breaks) are:
+ *   - `gpus` ranks share the data/context-parallel work of one pipeline
+ *     stage; a microbatch of cp size c occupies one slot on each rank of an
+ *     aligned group of c ranks; every rank runs m slots.
+ *   - workload w(S) = work_quad*S^2 + work_lin*S; a rank's share of a
+ *     sample under cp size c is w(S)/c and its memory is S tokens for c = 1,
+ *     else S rounded up to 2c equal chunks, over c (the zigzag split).
+ *   - quota W = total workload / (gpus * m) (Eq. 1-3 with equal m).
+ *   - stage 1: each sample gets the smallest power-of-two c <= max_cp with
+ *     share <= W and tokens <= mem_tokens (max_cp if the quota is never
+ *     met); samples with c > 1 open their own microbatch.
+ *   - stage 2: those microbatches, heaviest first, take the lightest
+ *     unsplit samples while quota and memory hold.
+ *   - stage 3: the remaining samples, heaviest first, go to the least-loaded
+ *     cp = 1 microbatch with room; there are gpus*m - sum(c) of those.
+ *   - placement: split microbatches, largest c first, on the free aligned
+ *     group of least load; cp = 1 microbatches on the least-loaded rank.
+ *   - step time: max over ranks of V*sum(slot shares) + (p-1)*max(slot
+ *     share), which is Eq. 1's W (m V + p - 1) for equal shares.
+ *   - m runs over [m_min, m_max] within knee_radius of the knee of the
+ *     budget curve max(total/(gpus m), max w / max_cp) (the point farthest
+ *     below the chord of the normalised curve); knee_radius < 0 searches
+ *     every m.  The least step time wins; ties go to the smaller m.
+ * Decisions are exact integer comparisons (the knee: IEEE double); ties go
+ * to the lower index, so the plan is a deterministic function of the input.
+ * Host memory only, thread-safe, no GPU involved. */
+typedef struct {
+    int32_t gpus;         /* ranks in the pool, 1..65536, a multiple of max_cp */
+    int32_t max_cp;       /* largest cp size, a power of two <= gpus */
+    int32_t pp;           /* pipeline stages p, 1..4096 */
+    int32_t vpp;          /* virtual stages per pipeline rank V, 1..4096 */
+    int64_t mem_tokens;   /* tokens one rank holds for one microbatch, >= 1 */
+    int64_t work_quad;    /* a in w(S) = a S^2 + b S, 0..2^16 */
+    int64_t work_lin;     /* b, 0..2^32; a + b > 0 */
+    int32_t m_min;        /* microbatches per rank searched: m_min..m_max, */
+    int32_t m_max;        /*   1 <= m_min <= m_max <= 4096, gpus*m_max <= 2^22 */
+    int32_t knee_radius;  /* search |m - knee| <= knee_radius; < 0: all m */
+} cpattn_dcp_config;
+
+/* Result arrays are caller-owned host memory. */
+typedef struct {
+    int32_t m;                /* out: chosen microbatches per rank */
+    int32_t knee;             /* out: knee of the budget curve */
+    int32_t num_buckets;      /* out: microbatches in the plan (<= gpus*m) */
+    double step_time;         /* out: modelled step time, workload units */
+    int32_t* sample_bucket;   /* [n]   microbatch of every sample */
+    int32_t* bucket_cp;       /* [cap] cp size */
+    int32_t* bucket_slot;     /* [cap] slot 0..m-1 */
+    int32_t* bucket_rank;     /* [cap] first rank of its group (a multiple of cp) */
+    int64_t* bucket_tokens;   /* [cap] tokens per rank */
+    double* bucket_load;      /* [cap] sum of w(S) over its samples */
+    double* times;            /* [m_max-m_min+1] step time per m; -1 infeasible,
+                                 -2 outside the knee's radius */
+    double* budget;           /* [m_max-m_min+1] budget curve */
+    int32_t bucket_capacity;  /* entries of the bucket arrays, >= gpus*m_max */
+} cpattn_dcp_plan;
+
+/* Plans lengths[n] (1 <= n <= 2^24, 1 <= length <= 2^22).  Microbatches are
+ * numbered split ones first (by workload, heaviest first), then the cp = 1
+ * ones.  INVALID_ARG on a bad argument; INFEASIBLE when no m in the range
+ * fits (a sample over the memory cap even at max_cp, or more split
+ * microbatches than grid cells). */
+cpattn_status cpattn_dcp_plan_batch(const int32_t* lengths, int32_t n, const cpattn_dcp_config* cfg,
+                                    cpattn_dcp_plan* out);
+
+/* Eq. 1-3 of the same section: per-microbatch workload quota W[i] of each of
+ * n data-parallel ranks running m[i] >= 1 microbatches, with V = vpp virtual
+ * stages and p = pp pipeline stages, such that every rank finishes together
+ * (W_i (m_i V + p - 1) equal) and sum_i W_i m_i = total.  Double precision;
+ * INVALID_ARG on a bad argument. */
+cpattn_status cpattn_dcp_quotas(const int32_t* m, int32_t n, int32_t vpp, int32_t pp, double total, double* W);
 
 #ifdef __cplusplus
 }
