@@ -255,6 +255,118 @@ def cpu_baseline(w, x, rows=256):
                       f"(query, key) pairs per head, fp64 NumPy"}
 
 
+def _static_cp_plan(lens, gpus, max_cp, mem):
+    """Packing-only baseline with a static cp: samples in batch order are
+    packed into microbatches of at most max_cp*mem tokens, every microbatch
+    split max_cp ways, and dealt round-robin to the gpus/max_cp groups."""
+    mbs, cur, tok = [], [], 0
+    for L in lens:
+        if cur and tok + L > max_cp * mem:
+            mbs.append(cur)
+            cur, tok = [], 0
+        cur.append(L)
+        tok += L
+    if cur:
+        mbs.append(cur)
+    groups = gpus // max_cp
+    return [(mb, max_cp, j % groups) for j, mb in enumerate(mbs)]
+
+
+def _time_rank_share(c, torch, pool, lens, cp, reps=2):
+    """ms of rank 0's attention for one microbatch (every sequence
+    zigzag-split over cp ranks): cp forward steps with merges, the backward
+    preprocess and cp backward steps.  Inputs are random; only time counts."""
+    import numpy as np
+    from context_attention_varlen_amd.ring import ForwardBuffers
+    loc = [L // cp for L in lens]
+    T = sum(loc)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(loc)]).astype(np.int32), device="cuda")
+    q, k, v, do = (pool[n][:T] for n in ("q", "k", "v", "do"))
+    dq, dk, dv, delta = pool["dq"][:T], pool["dk"][:T], pool["dv"][:T], pool["delta"][:, :T]
+    bufs = ForwardBuffers.make(q, T, len(lens))
+    steps = [c.make_step(cp, 0, s) for s in range(cp)]
+
+    def run():
+        bufs.reset()
+        for s in range(cp):
+            c.cpattn_fwd_step(q, k, v, cu, cu, len(lens), c.CAUSAL, steps[s], 0.0, bufs.out_partial,
+                              bufs.lse_partial, bufs.workspace)
+            c.cpattn_merge(bufs.out, bufs.lse, bufs.out_partial, bufs.lse_partial)
+        c.cpattn_bwd_preprocess(bufs.out, do, delta)
+        for s in range(cp):
+            c.cpattn_bwd_step(q, k, v, do, bufs.lse, delta, cu, cu, len(lens), c.CAUSAL, steps[s], 0.0,
+                              dq, dk, dv, bufs.workspace)
+    run()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def dynamic_cp_extra(c, torch, gen):
+    """Dynamic-CP plan of a long-tail global batch (host planner), scored by
+    the planner's model and by timing every microbatch's rank share on the
+    attention path, against a packing-only plan with a static cp."""
+    import time
+
+    import numpy as np
+
+    import workloads
+    lens = workloads.global_batch_lengths()
+    G, MAXCP, MEM, Hq, Hkv, d = 16, 8, 32768, 32, 8, 128
+    cfg = (G, MAXCP, 1, 1, MEM, 1, 0, 1, 8, -1)
+    reps = 20
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        plan = c.cpattn_dcp_plan_batch(lens, *cfg)
+    plan_ms = (time.perf_counter() - t0) / reps * 1e3
+    sb = plan["sample_bucket"]
+    dyn = [([lens[i] for i in np.flatnonzero(sb == j)], int(plan["cp"][j]), int(plan["rank"][j]))
+           for j in range(plan["num_buckets"])]
+    static = _static_cp_plan(lens, G, MAXCP, MEM)
+    pool = {n: torch.randn((MEM, Hq if n in ("q", "do") else Hkv, d), device="cuda", generator=gen).bfloat16()
+            for n in ("q", "k", "v", "do")}
+    pool.update({"dq": torch.zeros((MEM, Hq, d), device="cuda"), "dk": torch.zeros((MEM, Hkv, d), device="cuda"),
+                 "dv": torch.zeros((MEM, Hkv, d), device="cuda"), "delta": torch.zeros((Hq, MEM), device="cuda")})
+
+    def score(mbs, group_of):
+        rank_ms, rank_model = np.zeros(G), np.zeros(G)
+        meas, model = [], []
+        for lens_b, cp, first in mbs:
+            if not lens_b:
+                continue
+            ms = _time_rank_share(c, torch, pool, lens_b, cp)
+            w = sum(L * L for L in lens_b) / cp
+            for r in group_of(first, cp):
+                rank_ms[r] += ms
+                rank_model[r] += w
+            meas.append(ms)
+            model.append(w)
+        fit = np.polyfit(model, meas, 1)
+        r2 = 1 - np.sum((np.polyval(fit, model) - meas) ** 2) / np.sum((np.asarray(meas) - np.mean(meas)) ** 2)
+        return rank_ms, rank_model, r2
+
+    d_ms, d_model, d_r2 = score(dyn, lambda first, cp: range(first, first + cp))
+    s_ms, s_model, s_r2 = score(static, lambda g, cp: range(g * cp, (g + 1) * cp))
+    del pool
+    torch.cuda.empty_cache()
+    return {"samples": len(lens), "tokens": int(sum(lens)), "longest": int(max(lens)), "gpus": G, "max_cp": MAXCP,
+            "mem_tokens": MEM, "heads": [Hq, Hkv], "head_dim": d, "workload_model": "S^2",
+            "planner_ms": round(plan_ms, 3), "m": plan["m"], "knee": plan["knee"],
+            "microbatches": plan["num_buckets"],
+            "cp_sizes": {str(k): int(v) for k, v in zip(*np.unique(plan["cp"], return_counts=True))},
+            "model_step": float(d_model.max()), "model_static_step": float(s_model.max()),
+            "model_speedup": round(float(s_model.max() / d_model.max()), 3),
+            "measured_step_ms": round(float(d_ms.max()), 2), "measured_mean_rank_ms": round(float(d_ms.mean()), 2),
+            "measured_static_step_ms": round(float(s_ms.max()), 2),
+            "measured_static_mean_rank_ms": round(float(s_ms.mean()), 2),
+            "measured_speedup": round(float(s_ms.max() / d_ms.max()), 3),
+            "model_fit_r2": [round(float(d_r2), 4), round(float(s_r2), 4)]}
+
+
 def extras(c, torch):
     """Forward and merge figures of the other workloads (not part of `value`)."""
     import workloads
@@ -366,6 +478,7 @@ def extras(c, torch):
         "pct_peak_hbm": round(100 * nbytes / (hms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 1)}
     del src, loc
     torch.cuda.empty_cache()
+    out["dynamic_cp_global_batch"] = dynamic_cp_extra(c, torch, gen)
     return out
 
 

@@ -24,6 +24,12 @@ Workloads (the five shapes the library is measured and checked on):
                 over cp=3 ranks (4 time chunks per rank, 24960 local tokens),
                 rank 0; forward and backward.
 
+Dynamic-CP global batch (global_batch_lengths): 256 samples with
+lognormal(8.0, 1.2) lengths (median ~3000 tokens, a tail capped at 131072),
+rounded up to multiples of 16; it is planned into microbatches of per-sample
+cp size and each microbatch's rank share is timed on the attention path
+(Hq=32/Hkv=8, d=128, causal).
+
 Page context: the long-tail length mix stands in for the variable-length
 datasets of "Speeding up Variable-Length Training with Dynamic Context
 Parallelism and NVIDIA Megatron Core" (section A3, long-tail distribution);
@@ -116,6 +122,16 @@ def long_tail_lengths(rng: np.random.Generator, total: int, long_len: int,
         lens.append(length)
         rem -= length
     return lens
+
+
+def global_batch_lengths(seed: int = 0, n: int = 256, mu: float = 8.0, sigma: float = 1.2,
+                         cap: int = 131072, quantum: int = 16) -> list:
+    """A global batch of n sample lengths with a long tail: lognormal(mu,
+    sigma) tokens, rounded up to a multiple of ``quantum`` (so every sample
+    can be zigzag-split up to cp = quantum / 2) and capped at ``cap``."""
+    x = np.random.default_rng(seed).lognormal(mu, sigma, n)
+    lens = np.minimum(np.ceil(x / quantum).astype(np.int64) * quantum, cap)
+    return [int(v) for v in np.maximum(lens, quantum)]
 
 
 def _c2_lengths() -> tuple:
