@@ -338,18 +338,26 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
   const int nt0 = ceil_div(it.seg[0].n, BQ);
   const int nt1 = it.nseg > 1 ? ceil_div(it.seg[1].n, BQ) : 0;
   const int ntiles = (nt0 + nt1) * a.grp;
-  // Tiles run q-head by q-head, and within a head over segment 0 then 1;
-  // the position advances without division. Segment fields are picked by
-  // select so they stay in scalar registers.
+  // Query tiles run from the last segment's top tile downwards, and the
+  // q-heads of the GQA group innermost.  Every key tile of a sequence's
+  // chunk pair then starts on the same query rows and sweeps them in the
+  // same order, each stopping at its own diagonal, so the workgroups that
+  // run side by side on one XCD read each Q/dO tile from L2 at about the
+  // same time instead of each fetching its own rows.  The position
+  // advances without division; segment fields are picked by select so they
+  // stay in scalar registers.
   struct TilePos { int h, s, t0; };
   auto seg_n = [&](int sgi) { return sgi ? it.seg[1].n : it.seg[0].n; };
+  const int h_lo = g * a.grp, h_hi = h_lo + a.grp;
   auto next_pos = [&](TilePos tp) {
-    tp.t0 += BQ;
-    if (tp.t0 >= seg_n(tp.s)) {
-      tp.t0 = 0;
-      const bool to1 = tp.s == 0 && it.nseg > 1;
-      tp.h += to1 ? 0 : 1;
-      tp.s = to1 ? 1 : 0;
+    ++tp.h;
+    if (tp.h >= h_hi) {
+      tp.h = h_lo;
+      tp.t0 -= BQ;
+      if (tp.t0 < 0) {   // down to segment 0 (only reached from segment 1)
+        tp.s = 0;
+        tp.t0 = (nt0 - 1) * BQ;
+      }
     }
     return tp;
   };
@@ -367,7 +375,7 @@ __device__ __forceinline__ void bwd_dkv_body(const BwdArgs& a, int bid, uint16_t
                                                (__attribute__((address_space(3))) void*)dstl, 4, lane * 4, 0, 0, 0);
     }
   };
-  TilePos cur = {g * a.grp, 0, 0};  // tile being computed
+  TilePos cur = nt1 > 0 ? TilePos{h_lo, 1, (nt1 - 1) * BQ} : TilePos{h_lo, 0, (nt0 - 1) * BQ};  // tile computed
   TilePos nxt = next_pos(cur);      // tile loaded next
   issue(cur, 0);
 
