@@ -374,8 +374,9 @@ typedef struct {
 /* Plans lengths[n] (1 <= n <= 2^24, 1 <= length <= 2^22).  Microbatches are
  * numbered split ones first (by workload, heaviest first), then the cp = 1
  * ones.  INVALID_ARG on a bad argument; INFEASIBLE when no m in the range
- * fits (a sample over the memory cap even at max_cp, or more split
- * microbatches than grid cells). */
+ * yields a plan: a sample over the memory cap even at max_cp, split
+ * microbatches needing more cells than gpus*m, or unsplit samples that do
+ * not fit the memory of the cp = 1 microbatches left over. */
 cpattn_status cpattn_dcp_plan_batch(const int32_t* lengths, int32_t n, const cpattn_dcp_config* cfg,
                                     cpattn_dcp_plan* out);
 
