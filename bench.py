@@ -332,6 +332,8 @@ def dynamic_cp_extra(c, torch, gen):
     pool.update({"dq": torch.zeros((MEM, Hq, d), device="cuda"), "dk": torch.zeros((MEM, Hkv, d), device="cuda"),
                  "dv": torch.zeros((MEM, Hkv, d), device="cuda"), "delta": torch.zeros((Hq, MEM), device="cuda")})
 
+    samples = []     # (sum S^2 / cp, sum S / cp, ms) per timed microbatch share
+
     def score(mbs, group_of):
         rank_ms, rank_model = np.zeros(G), np.zeros(G)
         meas, model = [], []
@@ -345,12 +347,17 @@ def dynamic_cp_extra(c, torch, gen):
                 rank_model[r] += w
             meas.append(ms)
             model.append(w)
+            samples.append((w, sum(lens_b) / cp, ms))
         fit = np.polyfit(model, meas, 1)
         r2 = 1 - np.sum((np.polyval(fit, model) - meas) ** 2) / np.sum((np.asarray(meas) - np.mean(meas)) ** 2)
         return rank_ms, rank_model, r2
 
     d_ms, d_model, d_r2 = score(dyn, lambda first, cp: range(first, first + cp))
     s_ms, s_model, s_r2 = score(static, lambda g, cp: range(g * cp, (g + 1) * cp))
+    # calibration of w(S) = a S^2 + b S for this library on this shape:
+    # least squares of the measured share times on (sum S^2 / cp, sum S / cp)
+    A = np.asarray([[x[0], x[1]] for x in samples])
+    coef, *_ = np.linalg.lstsq(A, np.asarray([x[2] for x in samples]), rcond=None)
     del pool
     torch.cuda.empty_cache()
     return {"samples": len(lens), "tokens": int(sum(lens)), "longest": int(max(lens)), "gpus": G, "max_cp": MAXCP,
@@ -364,7 +371,8 @@ def dynamic_cp_extra(c, torch, gen):
             "measured_static_step_ms": round(float(s_ms.max()), 2),
             "measured_static_mean_rank_ms": round(float(s_ms.mean()), 2),
             "measured_speedup": round(float(s_ms.max() / d_ms.max()), 3),
-            "model_fit_r2": [round(float(d_r2), 4), round(float(s_r2), 4)]}
+            "model_fit_r2": [round(float(d_r2), 4), round(float(s_r2), 4)],
+            "calibrated_ns_per_S2": round(float(coef[0]) * 1e6, 6), "calibrated_ns_per_token": round(float(coef[1]) * 1e6, 3)}
 
 
 def extras(c, torch):
