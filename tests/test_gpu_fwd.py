@@ -98,6 +98,11 @@ SMALL = [
     ([2 * 4 * 100, 2 * 4 * 100], 1, 4, 2, 128, oracle.TF_BLOCK, (100, 4)),
     ([256, 128], 2, 4, 4, 64, oracle.CAUSAL, (0, 0)),
     ([200], 1, 2, 1, 64, oracle.TF_BLOCK, (25, 4)),
+    # tile counts around the two-tiles-per-trip loop of the pipelined forward:
+    # 16 key tiles with a partial last one, 3 + 3, and 1 + 11 at d = 64
+    ([1000, 24], 1, 2, 1, 128, oracle.CAUSAL, (0, 0)),
+    ([192, 130], 1, 2, 2, 128, oracle.BIDIR, (0, 0)),
+    ([64, 704], 1, 2, 2, 64, oracle.CAUSAL, (0, 0)),
 ]
 
 
