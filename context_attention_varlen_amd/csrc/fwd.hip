@@ -258,6 +258,10 @@ void fwd_bf16_kernel(FwdArgs a) {
     }
 #pragma unroll
     for (int x = 0; x < PF; ++x) read_op(more ? x : NS + x);
+    // Wave priority: the PV half of an iteration (whose second half carries
+    // the mask and row max of tile j + 1) issues ahead of a co-resident
+    // wave's S^T half (measured: +1 to +3 % over equal priority).
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
       if (more) {
@@ -267,6 +271,7 @@ void fwd_bf16_kernel(FwdArgs a) {
       slot_work(u);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
       if (m + PF < NP) read_v(m + PF);
