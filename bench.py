@@ -211,8 +211,26 @@ def run_hot_path(c, torch, w, steps, warmup):
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ok = bool(torch.isfinite(bufs.out).all().item()) and (not w.backward or bool(torch.isfinite(dq).all().item()))
     pairs = [c.cpattn_count_pairs(w.cu_seqlens, w.mask, st) for st in steps_]
-    # live partial rows per step (rows with at least one key), for merge bytes
-    return wall_ms, tm.stats(), pairs, ok, x
+    # after the timed region: the same step captured once as a HIP graph and
+    # replayed (every call only enqueues kernels, so it captures as is)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(null)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(null)
+    graph.replay()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ea.record()
+    for _ in range(steps):
+        graph.replay()
+    eb.record()
+    torch.cuda.synchronize()
+    graph_ms = ea.elapsed_time(eb) / steps
+    return wall_ms, tm.stats(), pairs, ok, x, graph_ms
 
 
 def cpu_baseline(w, x, rows=256):
@@ -519,7 +537,7 @@ def main():
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
-    wall_ms, st, pairs, finite, x = run_hot_path(c, torch, w, args.steps, args.warmup)
+    wall_ms, st, pairs, finite, x, graph_ms = run_hot_path(c, torch, w, args.steps, args.warmup)
     P = sum(pairs)
     fwd_flops = 4 * w.head_dim * w.heads_q * P
     bwd_flops = 10 * w.head_dim * w.heads_q * P if w.backward else 0
@@ -559,6 +577,10 @@ def main():
                    "parallelism": f"cp{w.cp} (one rank's share on one GPU)"},
         "pairs_per_head": P, "flops_per_step": fwd_flops + bwd_flops, "outputs_finite": finite,
         "per_call": per_call, "roofline": roofline,
+        # not `value`: the same step captured once as a HIP graph and replayed
+        # `steps` times after the timed region (no per-call launch gaps)
+        "graph_replay": {"ms_per_step": round(graph_ms, 4),
+                         "tflops": round((fwd_flops + bwd_flops) / (graph_ms * 1e-3) / 1e12, 2)},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x)
