@@ -211,17 +211,26 @@ def run_hot_path(c, torch, w, steps, warmup):
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ok = bool(torch.isfinite(bufs.out).all().item()) and (not w.backward or bool(torch.isfinite(dq).all().item()))
     pairs = [c.cpattn_count_pairs(w.cu_seqlens, w.mask, st) for st in steps_]
-    # after the timed region: the same step captured once as a HIP graph and
-    # replayed (every call only enqueues kernels, so it captures as is)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step(null)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step(null)
+    return wall_ms, tm.stats(), pairs, ok, x, graph_step_ms(torch, step, null, steps)
+
+
+def graph_step_ms(torch, step, null, steps):
+    """After the timed region: the same step captured once as a HIP graph and
+    replayed `steps` times (every call only enqueues kernels, so it captures
+    as is).  None if this torch build cannot capture."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(null)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(null)
+    except RuntimeError as e:
+        print(f"graph capture unavailable: {e}", file=sys.stderr, flush=True)
+        return None
     graph.replay()
     ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ea.record()
@@ -229,8 +238,7 @@ def run_hot_path(c, torch, w, steps, warmup):
         graph.replay()
     eb.record()
     torch.cuda.synchronize()
-    graph_ms = ea.elapsed_time(eb) / steps
-    return wall_ms, tm.stats(), pairs, ok, x, graph_ms
+    return ea.elapsed_time(eb) / steps
 
 
 def cpu_baseline(w, x, rows=256):
@@ -579,8 +587,8 @@ def main():
         "per_call": per_call, "roofline": roofline,
         # not `value`: the same step captured once as a HIP graph and replayed
         # `steps` times after the timed region (no per-call launch gaps)
-        "graph_replay": {"ms_per_step": round(graph_ms, 4),
-                         "tflops": round((fwd_flops + bwd_flops) / (graph_ms * 1e-3) / 1e12, 2)},
+        "graph_replay": None if graph_ms is None else {
+            "ms_per_step": round(graph_ms, 4), "tflops": round((fwd_flops + bwd_flops) / (graph_ms * 1e-3) / 1e12, 2)},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x)
