@@ -78,6 +78,17 @@ class Planner {
       total_ += s_[i].w;
       wmax_ = std::max(wmax_, s_[i].w);
     }
+    // the two orders every m uses: workload descending and ascending, both
+    // with ties by index ascending
+    desc_.resize(n);
+    for (int32_t i = 0; i < n; ++i) desc_[i] = i;
+    asc_ = desc_;
+    std::sort(desc_.begin(), desc_.end(), [&](int32_t a, int32_t b) {
+      return s_[a].w != s_[b].w ? s_[a].w > s_[b].w : a < b;
+    });
+    std::sort(asc_.begin(), asc_.end(), [&](int32_t a, int32_t b) {
+      return s_[a].w != s_[b].w ? s_[a].w < s_[b].w : a < b;
+    });
   }
 
   i128 total() const { return total_; }
@@ -98,18 +109,18 @@ class Planner {
     const int32_t n = (int32_t)s_.size();
     const i128 gm = (i128)cfg_.gpus * m;
     std::vector<int32_t> cps(n);
-    std::vector<int32_t> heavy, light;
     for (int32_t i = 0; i < n; ++i) {
       cps[i] = pick_cp(s_[i], m);
       if (cps[i] == 0) return false;
-      (cps[i] > 1 ? heavy : light).push_back(i);
     }
+    std::vector<int32_t> heavy, light;   // heaviest first; lightest first
+    for (int32_t i : desc_)
+      if (cps[i] > 1) heavy.push_back(i);
+    for (int32_t i : asc_)
+      if (cps[i] == 1) light.push_back(i);
     p.mbs.clear();
     p.owner.assign(n, -1);
     // stage 1: one microbatch per split sample, heaviest first
-    std::sort(heavy.begin(), heavy.end(), [&](int32_t a, int32_t b) {
-      return s_[a].w != s_[b].w ? s_[a].w > s_[b].w : a < b;
-    });
     int64_t split_cells = 0;
     for (int32_t i : heavy) {
       Mb mb{cps[i], s_[i].w, rank_tokens(s_[i].len, cps[i]), -1, -1, i};
@@ -118,9 +129,6 @@ class Planner {
       split_cells += cps[i];
     }
     // stage 2: top up with the lightest cp = 1 samples (ascending workload)
-    std::sort(light.begin(), light.end(), [&](int32_t a, int32_t b) {
-      return s_[a].w != s_[b].w ? s_[a].w < s_[b].w : a < b;
-    });
     size_t next = 0;
     for (size_t j = 0; j < p.mbs.size() && next < light.size(); ++j) {
       Mb& mb = p.mbs[j];
@@ -139,27 +147,34 @@ class Planner {
     if (ones < 0) return false;
     const size_t base = p.mbs.size();
     for (int64_t j = 0; j < ones; ++j) p.mbs.push_back(Mb{1, 0, 0, -1, -1, -1});
-    std::vector<int32_t> rest(light.begin() + next, light.end());
-    std::sort(rest.begin(), rest.end(), [&](int32_t a, int32_t b) {
-      return s_[a].w != s_[b].w ? s_[a].w > s_[b].w : a < b;
-    });
+    // the unsplit samples stage 2 left, heaviest first
+    std::vector<int32_t> rest;
+    for (int32_t i : desc_)
+      if (cps[i] == 1 && p.owner[i] < 0) rest.push_back(i);
     if (!rest.empty() && ones == 0) return false;
-    // min-heap on (load, index); entries popped without room are set aside
+    // Min-heap on (load, index).  A microbatch popped without room for the
+    // current sample is parked by its free room; samples come longest first,
+    // so it rejoins the heap only once a sample fits that room.  The heap
+    // top is then always the least-loaded microbatch with room.
     typedef std::pair<i128, int32_t> Key;
     std::priority_queue<Key, std::vector<Key>, std::greater<Key>> heap;
     for (int64_t j = 0; j < ones; ++j) heap.push(Key(0, (int32_t)(base + j)));
-    std::vector<Key> aside;
+    std::priority_queue<std::pair<int64_t, int32_t>> parked;   // (free room, index), largest room first
     for (int32_t i : rest) {
       const Sample& x = s_[i];
+      while (!parked.empty() && parked.top().first >= x.len) {
+        const int32_t b = parked.top().second;
+        parked.pop();
+        heap.push(Key(p.mbs[b].load, b));
+      }
       int32_t hit = -1;
       while (!heap.empty()) {
-        Key k = heap.top();
+        const Key k = heap.top();
         heap.pop();
-        if (p.mbs[k.second].tokens + x.len <= cfg_.mem_tokens) { hit = k.second; break; }
-        aside.push_back(k);
+        const int64_t room = cfg_.mem_tokens - p.mbs[k.second].tokens;
+        if (room >= x.len) { hit = k.second; break; }
+        parked.push(std::make_pair(room, k.second));
       }
-      for (const Key& k : aside) heap.push(k);
-      aside.clear();
       if (hit < 0) return false;
       Mb& mb = p.mbs[hit];
       mb.load += x.w;
@@ -199,24 +214,37 @@ class Planner {
       if (x.load != y.load) return x.load > y.load;
       return x.first < y.first;
     });
+    // The choice is the least (max rank load of the group, slot, group)
+    // over every aligned group with a free slot.  Split microbatches come
+    // largest cp first, so the taken cells of a slot form aligned blocks at
+    // least as large as the current one: an aligned block of the current
+    // size is wholly free or wholly taken, its first cell tells which, and a
+    // group's best slot is its lowest free one (a pointer that only moves up
+    // while the size stays the same).
+    int32_t cur_c = 0;
+    std::vector<int32_t> group_free;
     for (size_t j : order) {
       Mb& mb = p.mbs[j];
-      const int32_t c = mb.cp;
-      bool found = false;
+      const int32_t c = mb.cp, ng = G / c;
+      if (c != cur_c) {
+        cur_c = c;
+        group_free.assign(ng, 0);
+      }
+      int32_t bg = -1, bk = 0;
       i128 best = 0;
-      int32_t bk = 0, bg = 0;
-      for (int32_t k = 0; k < m; ++k) {
-        for (int32_t g = 0; g < G / c; ++g) {
-          bool free_ = true;
-          i128 mxl = 0;
-          for (int32_t r = g * c; r < (g + 1) * c; ++r) {
-            if (used[(size_t)k * G + r]) { free_ = false; break; }
-            mxl = std::max(mxl, load[r]);
-          }
-          if (free_ && (!found || mxl < best)) { found = true; best = mxl; bk = k; bg = g; }
+      for (int32_t g = 0; g < ng; ++g) {
+        int32_t& k = group_free[g];
+        while (k < m && used[(size_t)k * G + (size_t)g * c]) ++k;
+        if (k == m) continue;
+        i128 mxl = 0;
+        for (int32_t r = g * c; r < (g + 1) * c; ++r) mxl = std::max(mxl, load[r]);
+        if (bg < 0 || mxl < best || (mxl == best && k < bk)) {
+          bg = g;
+          bk = k;
+          best = mxl;
         }
       }
-      if (!found) return false;
+      if (bg < 0) return false;
       mb.slot = bk;
       mb.rank = bg * c;
       const i128 share = mb.load * (cfg_.max_cp / c);
@@ -257,6 +285,7 @@ class Planner {
 
   cpattn_dcp_config cfg_;
   std::vector<Sample> s_;
+  std::vector<int32_t> desc_, asc_;
   i128 total_, wmax_;
 };
 

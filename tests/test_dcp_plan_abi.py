@@ -71,6 +71,16 @@ def test_plan_long_tail_batch():
     assert r is not None and max(r["cp"]) == 8
 
 
+@pytest.mark.parametrize("mem,gpus,lo,hi", [(16384, 64, 4, 16), (32768, 64, 2, 12), (20000, 128, 2, 10)])
+def test_plan_larger_batch(mem, gpus, lo, hi):
+    """1500 long-tail samples (9.1M tokens): infeasible and feasible m side by
+    side, memory-bound cp = 1 microbatches (the least-loaded one often lacks
+    room), many split microbatches of every size."""
+    lens = workloads.global_batch_lengths(seed=3, n=1500)
+    r = _compare(lens, gpus, 8, 2, 1, mem, 1, 0, lo, hi, -1)
+    assert r is not None and set(r["cp"]) == {1, 2, 4, 8}
+
+
 @pytest.mark.parametrize("lengths,cfg", [
     ([1], (1, 1, 1, 1, 1, 1, 0, 1, 1, -1)),                    # smallest problem
     ([5, 5, 5, 5], (2, 2, 1, 1, 10, 1, 0, 1, 3, -1)),          # ties everywhere
