@@ -44,7 +44,7 @@ namespace {
 
 typedef __int128 i128;
 
-struct Sample { int64_t len; i128 w; int32_t idx; };
+struct Sample { int64_t len; i128 w; };
 
 struct Mb {
   int32_t cp;
@@ -74,7 +74,7 @@ class Planner {
     wmax_ = 0;
     for (int32_t i = 0; i < n; ++i) {
       const int64_t S = lengths[i];
-      s_[i] = {S, (i128)cfg.work_quad * S * S + (i128)cfg.work_lin * S, i};
+      s_[i] = {S, (i128)cfg.work_quad * S * S + (i128)cfg.work_lin * S};
       total_ += s_[i].w;
       wmax_ = std::max(wmax_, s_[i].w);
     }
@@ -185,7 +185,7 @@ class Planner {
     return place(p, m, base);
   }
 
-  i128 simulate(const Plan& p, int32_t m) const {
+  i128 simulate(const Plan& p) const {
     const int32_t G = cfg_.gpus;
     std::vector<i128> sum(G, 0), mx(G, 0);
     for (const Mb& mb : p.mbs) {
@@ -195,7 +195,6 @@ class Planner {
         mx[r] = std::max(mx[r], share);
       }
     }
-    (void)m;
     i128 t = 0;
     for (int32_t r = 0; r < G; ++r) t = std::max(t, (i128)cfg_.vpp * sum[r] + (i128)(cfg_.pp - 1) * mx[r]);
     return t;
@@ -353,7 +352,7 @@ CPATTN_API cpattn_status cpattn_dcp_plan_batch(const int32_t* lengths, int32_t n
     const int32_t mj = c.m_min + j;
     if (c.knee_radius >= 0 && std::abs(mj - knee) > c.knee_radius) { out->times[j] = -2.0; continue; }
     if (!pl.build(mj, cur)) { out->times[j] = -1.0; continue; }
-    cur.time = pl.simulate(cur, mj);
+    cur.time = pl.simulate(cur);
     out->times[j] = (double)cur.time / c.max_cp;
     if (best_m < 0 || cur.time < best.time) { std::swap(best, cur); best_m = mj; }
   }
