@@ -209,14 +209,20 @@ def run_hot_path(c, torch, w, steps, warmup):
         step(null)
     torch.cuda.synchronize()
     tm = Timer(torch)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(steps):
+    marks[0].record()
+    for i in range(steps):
         step(tm)
+        marks[i + 1].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    spread = {"median": round(step_ms[steps // 2] if steps % 2 else (step_ms[steps // 2 - 1] + step_ms[steps // 2]) / 2, 4),
+              "min": round(step_ms[0], 4), "max": round(step_ms[-1], 4)}
     ok = bool(torch.isfinite(bufs.out).all().item()) and (not w.backward or bool(torch.isfinite(dq).all().item()))
     pairs = [c.cpattn_count_pairs(w.cu_seqlens, w.mask, st) for st in steps_]
-    return wall_ms, tm.stats(), pairs, ok, x, graph_step_ms(torch, step, null, steps)
+    return wall_ms, tm.stats(), pairs, ok, x, graph_step_ms(torch, step, null, steps), spread
 
 
 def graph_step_ms(torch, step, null, steps):
@@ -550,7 +556,7 @@ def main():
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
-    wall_ms, st, pairs, finite, x, graph_ms = run_hot_path(c, torch, w, args.steps, args.warmup)
+    wall_ms, st, pairs, finite, x, graph_ms, spread = run_hot_path(c, torch, w, args.steps, args.warmup)
     P = sum(pairs)
     fwd_flops = 4 * w.head_dim * w.heads_q * P
     bwd_flops = 10 * w.head_dim * w.heads_q * P if w.backward else 0
@@ -580,6 +586,7 @@ def main():
         "metric": "blockwise attn TFLOP/s (causal-adjusted) + % of bf16 MFMA peak, 1 MI355X",
         "value": round(tflops, 2), "unit": "TFLOP/s", "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
+        "step_ms_events": spread,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16; long-tail lengths drawn as in workloads/)",
         "config": {"workload": f"{w.name}: {w.tokens} tokens ({len(w.seqlens)} sequences, longest "
