@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--workload", default="long_tail")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the graph-replay figure (counter runs: only the timed steps dispatch)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a device copy of a known size (reference for HBM byte counters)")
     p.add_argument("--write-traffic", nargs=4, metavar=("CAL_FETCH", "CAL_WRITE", "RUN_FETCH", "RUN_WRITE"),
@@ -131,7 +133,7 @@ def write_traffic(cal_fetch, cal_write, run_fetch, run_write):
     rec = {"_comment": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), "
                        f"scaled by what each counter reads for a 1 GiB device copy (bench.py --copy-calibration): "
                        f"FETCH_SIZE x {scales[0]:.3f}, WRITE_SIZE x {scales[1]:.3f}. Workload: bench.py "
-                       "--no-cpu-baseline --no-extras --steps 2 --warmup 0 (long_tail, 4 ring steps); "
+                       "--no-cpu-baseline --no-extras --no-graph --steps 2 --warmup 0 (long_tail, 4 ring steps); "
                        "the first step's launches are listed.",
            "read_scale": round(scales[0], 4), "write_scale": round(scales[1], 4)}
     fetch = _counter_rows(run_fetch, "FETCH_SIZE")
@@ -153,7 +155,7 @@ def write_traffic(cal_fetch, cal_write, run_fetch, run_write):
     print(path)
 
 
-def run_hot_path(c, torch, w, steps, warmup):
+def run_hot_path(c, torch, w, steps, warmup, graph=True):
     import numpy as np
 
     import workloads
@@ -222,7 +224,7 @@ def run_hot_path(c, torch, w, steps, warmup):
               "min": round(step_ms[0], 4), "max": round(step_ms[-1], 4)}
     ok = bool(torch.isfinite(bufs.out).all().item()) and (not w.backward or bool(torch.isfinite(dq).all().item()))
     pairs = [c.cpattn_count_pairs(w.cu_seqlens, w.mask, st) for st in steps_]
-    return wall_ms, tm.stats(), pairs, ok, x, graph_step_ms(torch, step, null, steps), spread
+    return wall_ms, tm.stats(), pairs, ok, x, graph_step_ms(torch, step, null, steps) if graph else None, spread
 
 
 def graph_step_ms(torch, step, null, steps):
@@ -556,7 +558,8 @@ def main():
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
-    wall_ms, st, pairs, finite, x, graph_ms, spread = run_hot_path(c, torch, w, args.steps, args.warmup)
+    wall_ms, st, pairs, finite, x, graph_ms, spread = run_hot_path(c, torch, w, args.steps, args.warmup,
+                                                                   graph=not args.no_graph)
     P = sum(pairs)
     fwd_flops = 4 * w.head_dim * w.heads_q * P
     bwd_flops = 10 * w.head_dim * w.heads_q * P if w.backward else 0

@@ -62,7 +62,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& a, int bid, uint16_t*
   uint16_t (*s_v)[BN * D] = (uint16_t (*)[BN * D])(smem + 2 * BN * D);
 
   int item_rank, h, g;
-  map_block(bid, a.grp, a.hkv, item_rank, h, g);
+  map_block(bid, a.grp, a.hkv, item_rank, h, g, items_per_unit(a.grp));
   if (item_rank >= a.hdr_q->n_items) return;
   const WorkItem it = a.items_q[a.order_q[item_rank]];
   if (it.nseg == 0) return;
@@ -633,7 +633,7 @@ hipError_t launch_bwd(BwdArgs a, bool bf16, int d, int64_t max_items_q, int64_t 
   const unsigned gk = unit_grid(max_items_k, a.hkv, 1);
   if (bf16) {
     a.dkv_blocks = (int)gk;
-    const dim3 grid(gk + gq);
+    const dim3 grid(gk + unit_grid(max_items_q, a.hkv, a.grp, items_per_unit(a.grp)));
     if (d == 128) hipLaunchKernelGGL(bwd_bf16_kernel<128>, grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(bwd_bf16_kernel<64>, grid, dim3(256), 0, stream, a);
   } else {

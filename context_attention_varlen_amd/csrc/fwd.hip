@@ -71,7 +71,7 @@ void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][BN * D];
 
   int item_rank, h, g;
-  map_block(blockIdx.x, a.grp, a.hkv, item_rank, h, g);
+  map_block(blockIdx.x, a.grp, a.hkv, item_rank, h, g, items_per_unit(a.grp));
   if (item_rank >= a.hdr->n_items) return;
   const WorkItem it = a.items[a.order[item_rank]];
 
@@ -368,7 +368,7 @@ constexpr int kFwdTile = 32 * kFwdWaves;   // query rows per workgroup
 int fwd_tile_rows(bool bf16) { return bf16 ? kFwdTile : 64; }
 
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream) {
-  const dim3 grid(unit_grid(max_items, a.hkv, a.grp));
+  const dim3 grid(unit_grid(max_items, a.hkv, a.grp, bf16 ? items_per_unit(a.grp) : 1));
   if (bf16) {
     if (d == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdWaves>), grid, dim3(64 * kFwdWaves), 0, stream, a);
     else hipLaunchKernelGGL((fwd_bf16_kernel<64, kFwdWaves>), grid, dim3(64 * kFwdWaves), 0, stream, a);

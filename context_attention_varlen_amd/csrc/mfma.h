@@ -192,19 +192,32 @@ __device__ __forceinline__ bf16x8 pack_b(const f32x16& c, int half) {
 // of one XCD (slots go round-robin over the 8 XCDs), and units are dealt to
 // XCDs in item order, so each XCD works on a fixed set of kv-heads when Hkv
 // divides 8 or 8 divides Hkv: their K/V stay in that XCD's L2.
-__device__ __forceinline__ void map_block(int bid, int grp, int hkv, int& item_rank, int& head, int& kvh) {
+// A unit is `rep` consecutive items (longest-first order) times the grp
+// q-heads of one kv-head, on consecutive slots of one XCD, so its workgroups
+// start together and stream the same K/V tiles through that XCD's L2.  A
+// GQA group of 4 or more q-heads already gives that sharing (rep = 1); with
+// fewer (MHA) a unit takes several query tiles of the same head instead:
+// on the teacher-forcing DiT shape (24 heads, MHA) this cut the forward's
+// HBM fetch from 63 GB to 23 GB per launch and sped it up by ~4.5 %.
+__host__ __device__ inline int items_per_unit(int grp) { return grp >= 4 ? 1 : (32 + grp - 1) / grp; }
+
+__device__ __forceinline__ void map_block(int bid, int grp, int hkv, int& item_rank, int& head, int& kvh,
+                                          int rep = 1) {
   const int x = bid & 7;
   const int k = bid >> 3;
-  const int u = k / grp, j = k - u * grp;
+  const int P = grp * rep;
+  const int u = k / P, j = k - u * P;
   const int U = u * 8 + x;
-  item_rank = U / hkv;
-  kvh = U - item_rank * hkv;
-  head = kvh * grp + j;
+  const int iu = U / hkv;
+  kvh = U - iu * hkv;
+  const int jr = j / grp;
+  item_rank = iu * rep + jr;
+  head = kvh * grp + (j - jr * grp);
 }
 
-inline unsigned unit_grid(int64_t max_items, int hkv, int grp) {
-  const int64_t units = max_items * hkv;
-  return (unsigned)(((units + 7) / 8) * 8 * grp);
+inline unsigned unit_grid(int64_t max_items, int hkv, int grp, int rep = 1) {
+  const int64_t units = (max_items + rep - 1) / rep * hkv;
+  return (unsigned)(((units + 7) / 8) * 8 * grp * rep);
 }
 
 }  // namespace cpattn
