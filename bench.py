@@ -32,6 +32,11 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 
 
+def note(msg):
+    """One progress line on stderr per finished phase (the JSON line stays alone on stdout)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -451,6 +456,7 @@ def extras(c, torch):
         tfl = 4 * w.head_dim * w.heads_q * pairs / (ms * 1e-3) / 1e12
         out[name] = {"fwd_ms": round(ms, 3), "fwd_tflops": round(tfl, 1),
                      "pct_peak": round(100 * tfl / PEAK_BF16_TFLOPS, 1), "pairs_per_head": pairs}
+        note(f"extra {name} forward done")
         if w.backward:
             do = partition(mk(w.heads_q), plan)
             dq = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
@@ -525,7 +531,9 @@ def extras(c, torch):
         "pct_peak_hbm": round(100 * nbytes / (hms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 1)}
     del src, loc
     torch.cuda.empty_cache()
+    note("exchange extras done")
     out["dynamic_cp_global_batch"] = dynamic_cp_extra(c, torch, gen)
+    note("dynamic-cp extra done")
     return out
 
 
@@ -560,6 +568,7 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     wall_ms, st, pairs, finite, x, graph_ms, spread = run_hot_path(c, torch, w, args.steps, args.warmup,
                                                                    graph=not args.no_graph)
+    note(f"timed region done ({args.steps} steps)")
     P = sum(pairs)
     fwd_flops = 4 * w.head_dim * w.heads_q * P
     bwd_flops = 10 * w.head_dim * w.heads_q * P if w.backward else 0
@@ -607,6 +616,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x)
+        note("cpu baseline done")
     if not args.no_extras:
         rec["extras"] = extras(c, torch)
     print(json.dumps(rec), flush=True)

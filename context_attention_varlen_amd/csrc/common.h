@@ -208,6 +208,8 @@ struct PartArgs {
   int scatter;                              // 0: global -> local, 1: local -> global
   int tf_b, tf_n;                           // > 0: balanced teacher-forcing split
   int hw_h, hw_w, hw_sh, hw_sw;             // > 0: height/width split of frames x H x W tokens
+  int cpr_shift;                            // log2(row_bytes / 16), set at launch
+  int tok_per_block;                        // local rows per workgroup, set at launch
 };
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);
@@ -218,7 +220,7 @@ int bwd_dkv_tile_rows(bool bf16);
 hipError_t launch_bwd(BwdArgs a, bool bf16, int d, int64_t max_items_q, int64_t max_items_k, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_delta(const DeltaArgs& a, hipStream_t stream);
-hipError_t launch_partition(const PartArgs& a, hipStream_t stream);
+hipError_t launch_partition(PartArgs a, hipStream_t stream);
 
 // Copy of `tokens` rows x `heads` heads between two THD tensors, starting at
 // (src_row0, src_h0) and (dst_row0, dst_h0): the one-device form of the

@@ -149,22 +149,21 @@ hipError_t launch_delta(const DeltaArgs& a, hipStream_t stream) {
 // Parallelism", section 4) local row o of a sequence is, with m = N/cp time
 // chunks per rank, row o mod B of the rank's (o/B mod m)-th time chunk in the
 // clean stream (o < mB) or the noisy stream.
-// One thread moves 16 bytes; the rows of a (token, head) are contiguous.
+// A workgroup moves the rows of a few consecutive local tokens: their global
+// rows are resolved once per token (binary search over cu_seqlens) into LDS,
+// then every thread keeps kPartK 16-byte nontemporal loads in flight over the
+// (token, head, 16-byte chunk) triples; the rows of a (token, head) are
+// contiguous, so consecutive threads touch consecutive bytes.
 // ---------------------------------------------------------------------------
 
+constexpr int kPartThreads = 256;
+constexpr int kPartK = 8;                                  // 16-byte chunks in flight per thread
+constexpr int kPartMaxTok = kPartThreads;                  // local rows per workgroup, at most
 
-__global__ __launch_bounds__(256) void partition_kernel(PartArgs a) {
-  const int cpr = a.row_bytes >> 4;                 // 16-byte chunks per (token, head)
-  const int64_t per_tok = (int64_t)cpr * a.heads;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t t = gid / per_tok;
-  if (t >= a.local_tokens) return;
-  const int64_t rem = gid - t * per_tok;
-  const int h = (int)(rem / cpr);
-  const int c = (int)(rem - (int64_t)h * cpr);
-  // rows past the last sequence, or a cu_seqlens array that points outside
-  // the global tensor, move nothing
-  if ((int64_t)a.cu[a.nseq] <= t * a.cp) return;
+// Global row of local row t, or -1 when the row moves nothing (past the last
+// sequence, or a cu_seqlens array that points outside the global tensor).
+__device__ int64_t part_global_row(const PartArgs& a, int64_t t) {
+  if ((int64_t)a.cu[a.nseq] <= t * a.cp) return -1;
   int64_t g = t;
   if (a.cp > 1) {
     // last b with cu[b] <= t*cp
@@ -198,17 +197,55 @@ __global__ __launch_bounds__(256) void partition_kernel(PartArgs a) {
       g = gb + (o < C ? (int64_t)a.rank * C + o : (int64_t)(2 * a.cp - 1 - a.rank) * C + (o - C));
     }
   }
-  if (g < 0 || g >= a.global_tokens) return;
-  const int64_t ls = a.scatter ? t : g;   // source row
-  const int64_t ld = a.scatter ? g : t;   // destination row
-  const u32x4 v = ld_nt((const u32x4*)(a.src + ls * a.src_st + h * a.src_sh + c * 16));
-  st_nt(v, (u32x4*)(a.dst + ld * a.dst_st + h * a.dst_sh + c * 16));
+  return (g < 0 || g >= a.global_tokens) ? -1 : g;
 }
 
-hipError_t launch_partition(const PartArgs& a, hipStream_t stream) {
-  const int64_t threads = a.local_tokens * a.heads * (a.row_bytes >> 4);
-  if (threads == 0) return hipSuccess;
-  hipLaunchKernelGGL(partition_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
+__global__ __launch_bounds__(kPartThreads) void partition_kernel(PartArgs a) {
+  __shared__ int64_t s_row[kPartMaxTok];
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * a.tok_per_block;
+  const int ntok = (int)min((int64_t)a.tok_per_block, a.local_tokens - t0);
+  if (tid < ntok) s_row[tid] = part_global_row(a, t0 + tid);
+  __syncthreads();
+  const int cmask = (1 << a.cpr_shift) - 1;
+  const unsigned per_tok = (unsigned)a.heads << a.cpr_shift;   // 16-byte chunks per token
+  const unsigned total = (unsigned)ntok * per_tok;
+  for (unsigned base = 0; base < total; base += kPartThreads * kPartK) {
+    u32x4 v[kPartK];
+    int64_t dofs[kPartK];
+#pragma unroll
+    for (int k = 0; k < kPartK; ++k) {
+      const unsigned i = base + k * kPartThreads + tid;
+      dofs[k] = -1;
+      if (i < total) {
+        const unsigned tt = i / per_tok, rem = i - tt * per_tok;
+        const int h = (int)(rem >> a.cpr_shift), c = (int)(rem & cmask);
+        const int64_t g = s_row[tt];
+        if (g >= 0) {
+          const int64_t t = t0 + tt;
+          const int64_t ls = a.scatter ? t : g;   // source row
+          const int64_t ld = a.scatter ? g : t;   // destination row
+          v[k] = ld_nt((const u32x4*)(a.src + ls * a.src_st + h * a.src_sh + c * 16));
+          dofs[k] = ld * a.dst_st + h * a.dst_sh + c * 16;
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPartK; ++k)
+      if (dofs[k] >= 0) st_nt(v[k], (u32x4*)(a.dst + dofs[k]));
+  }
+}
+
+hipError_t launch_partition(PartArgs a, hipStream_t stream) {
+  if (a.local_tokens <= 0 || a.heads <= 0) return hipSuccess;
+  int shift = 0;
+  while ((16 << shift) < a.row_bytes) ++shift;
+  if ((16 << shift) != a.row_bytes) return hipErrorInvalidValue;   // rows are 128, 256 or 512 bytes
+  a.cpr_shift = shift;
+  const int64_t per_tok = (int64_t)a.heads << shift;
+  a.tok_per_block = (int)std::max<int64_t>(1, std::min<int64_t>(kPartMaxTok, kPartThreads * kPartK / per_tok));
+  const int64_t blocks = (a.local_tokens + a.tok_per_block - 1) / a.tok_per_block;
+  hipLaunchKernelGGL(partition_kernel, dim3((unsigned)blocks), dim3(kPartThreads), 0, stream, a);
   return hipGetLastError();
 }
 

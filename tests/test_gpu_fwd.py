@@ -54,6 +54,29 @@ def test_partition_bitexact_and_roundtrip(cpa, dtype, lens, cp):
     assert torch.equal(back.cpu(), g.cpu())
 
 
+@pytest.mark.parametrize("dtype,heads,d", [("bf16", 28, 128), ("f32", 80, 128), ("bf16", 1, 64), ("f32", 7, 64)])
+def test_partition_rows_per_workgroup(cpa, dtype, heads, d):
+    """Gather and scatter where a workgroup holds one row (80 fp32 heads: 2560
+    16-byte chunks, two passes), a few rows (28 heads) or many (1 head), with
+    a partial last workgroup: bit-exact against the index map."""
+    from context_attention_varlen_amd.ring import RankPlan, partition
+    lens = [392, 0, 56, 8 * 37]
+    cp = 4
+    rng = np.random.default_rng(5)
+    T = sum(lens)
+    g = dev(rng.standard_normal((T, heads, d), dtype=np.float32), tdtype(dtype))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    back = torch.zeros_like(g)
+    for r in range(cp):
+        plan = RankPlan.make(cu, cp, r)
+        _, l2g, _, _ = oracle.local_rows(cu, cp, r)
+        loc = partition(g, plan)
+        assert torch.equal(loc.cpu(), g.cpu()[torch.from_numpy(l2g)])
+        cpa.cpattn_unpartition(loc, back, plan.cu_global_dev, plan.num_seqs, cp, r)
+    torch.cuda.synchronize()
+    assert torch.equal(back.cpu(), g.cpu())
+
+
 def _run_ring(cpa, x, cu, cp, r, mode, dtype, hq, hkv, tf=(0, 0), keep=True):
     from context_attention_varlen_amd.ring import RankPlan, partition, ring_forward
     plan = RankPlan.make(cu, cp, r)
