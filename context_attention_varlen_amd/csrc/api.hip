@@ -589,8 +589,7 @@ CPATTN_API cpattn_status cpattn_bwd_step(const cpattn_tensor* q, const cpattn_te
   a.hdr_q = sq.hdr; a.items_q = sq.items; a.order_q = sq.order;
   a.hdr_k = sk.hdr; a.items_k = sk.items; a.order_k = sk.order;
   clear_stale_error();
-  if ((st = hip_status(launch_sched(sq, s))) != CPATTN_OK) return st;
-  if ((st = hip_status(launch_sched(sk, s))) != CPATTN_OK) return st;
+  if ((st = hip_status(launch_sched_pair(sq, sk, s))) != CPATTN_OK) return st;
   if (nseq == 0 || q->tokens == 0 || k->tokens == 0) return CPATTN_OK;
   return hip_status(launch_bwd(a, bf16, d, mq, mk, s));
 }

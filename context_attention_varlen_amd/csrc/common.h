@@ -213,6 +213,7 @@ struct PartArgs {
 };
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);
+hipError_t launch_sched_pair(const SchedArgs& a, const SchedArgs& b, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream);
 int fwd_tile_rows(bool bf16);
 int bwd_dq_tile_rows(bool bf16);

@@ -13,7 +13,8 @@
 //     never visited, and rows allowed for the whole tile are marked so the
 //     attention kernels skip the element mask there;
 //   * items sorted by cost, longest first, so long sequences start early.
-// It runs as a single 1024-thread workgroup and also validates the device
+// Each schedule is one 1024-thread workgroup (the backward builds its two
+// lists in one launch, one workgroup each); it also validates the device
 // cu_seqlens arrays (a bad array yields zero items and an error status).
 #include "common.h"
 
@@ -199,7 +200,7 @@ __device__ void build_item_tf(const SchedArgs& a, int pr0, int sr0, int t_in_seq
   it.nseg = ns;
 }
 
-__global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
+__device__ __forceinline__ void sched_body(const SchedArgs& a) {
   __shared__ int s_err;
   __shared__ int s_wave[kThreads / 64 + 1];
   __shared__ int s_bins[kBins];
@@ -337,10 +338,24 @@ __global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kThreads) void sched_kernel(SchedArgs a) { sched_body(a); }
+
+// Two independent schedules (disjoint workspace regions) in one launch, one
+// workgroup each: the backward's query-tile and key-tile lists.
+__global__ __launch_bounds__(kThreads) void sched_pair_kernel(SchedArgs a, SchedArgs b) {
+  if (blockIdx.x == 0) sched_body(a);
+  else sched_body(b);
+}
+
 }  // namespace
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sched_pair(const SchedArgs& a, const SchedArgs& b, hipStream_t stream) {
+  hipLaunchKernelGGL(sched_pair_kernel, dim3(2), dim3(kThreads), 0, stream, a, b);
   return hipGetLastError();
 }
 
