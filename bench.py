@@ -259,7 +259,7 @@ def graph_step_ms(torch, step, null, steps):
     return ea.elapsed_time(eb) / steps
 
 
-def cpu_baseline(w, x, rows=256):
+def cpu_baseline(w, x, rows=512):
     """The oracle, as it stands, on a bounded sample of the same workload:
     `rows` seeded query rows of the rank (all q-heads), forward and backward
     against every key they may attend."""
@@ -614,6 +614,13 @@ def main():
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": round(graph_ms, 4), "tflops": round((fwd_flops + bwd_flops) / (graph_ms * 1e-3) / 1e12, 2)},
     }
+    # the box's own figures: CU count and peak shader clock, and the dense
+    # bf16 matrix-core peak they give (4096 FLOP per clock per CU on gfx950)
+    cus, khz = c.cpattn_device_info(torch.cuda.current_device())
+    rec["device"] = {"name": torch.cuda.get_device_properties(0).name,
+                     "arch": torch.cuda.get_device_properties(0).gcnArchName, "cus": cus,
+                     "peak_clock_mhz": khz / 1000,
+                     "bf16_peak_at_peak_clock_tflops": round(cus * 4096 * khz * 1e3 / 1e12, 1)}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x)
         note("cpu baseline done")

@@ -25,7 +25,7 @@ F32, BF16 = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_INFEASIBLE = 0, 1, 2, 3, 4, 5
 
 EXPORTS = (
-    "cpattn_version", "cpattn_status_string", "cpattn_last_hip_error", "cpattn_partition_index", "cpattn_partition",
+    "cpattn_version", "cpattn_status_string", "cpattn_last_hip_error", "cpattn_device_info", "cpattn_partition_index", "cpattn_partition",
     "cpattn_unpartition", "cpattn_partition_index_tf", "cpattn_partition_tf", "cpattn_unpartition_tf",
     "cpattn_seq_to_head", "cpattn_head_to_seq", "cpattn_split_hw", "cpattn_partition_index_hw",
     "cpattn_partition_hw", "cpattn_unpartition_hw",
@@ -87,6 +87,7 @@ def _load():
         "cpattn_version": (ctypes.c_char_p, []),
         "cpattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "cpattn_last_hip_error": (ctypes.c_char_p, []),
+        "cpattn_device_info": (ctypes.c_int, [I32, P, P]),
         "cpattn_partition_index": (ctypes.c_int, [P, I32, I32, I32, P, P]),
         "cpattn_partition": (ctypes.c_int, [TP, TP, P, I32, I32, I32, P]),
         "cpattn_unpartition": (ctypes.c_int, [TP, TP, P, I32, I32, I32, P]),
@@ -169,6 +170,13 @@ def make_step(cp, rank, step, tf_chunk_tokens=0, tf_num_chunks=0) -> Step:
 # ---------------------------------------------------------------------------
 def cpattn_version() -> str:
     return _lib.cpattn_version().decode()
+
+
+def cpattn_device_info(device: int = 0):
+    """(compute units, peak shader clock in kHz) of a HIP device."""
+    cus, khz = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(_lib.cpattn_device_info(int(device), ctypes.byref(cus), ctypes.byref(khz)), "cpattn_device_info")
+    return cus.value, khz.value
 
 
 def cpattn_partition_index(cu_seqlens_global, cp: int, rank: int, with_map: bool = True):

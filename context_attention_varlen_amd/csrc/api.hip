@@ -129,6 +129,18 @@ CPATTN_API const char* cpattn_version(void) { return "cpattn 0.1 (gfx950)"; }
 
 CPATTN_API const char* cpattn_last_hip_error(void) { return g_last_hip_error; }
 
+CPATTN_API cpattn_status cpattn_device_info(int32_t device, int32_t* cu_count, int32_t* clock_khz) {
+  if (device < 0 || !cu_count || !clock_khz) return CPATTN_ERR_INVALID_ARG;
+  int cus = 0, khz = 0;
+  cpattn_status st;
+  if ((st = hip_status(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device))) != CPATTN_OK)
+    return st;
+  if ((st = hip_status(hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, device))) != CPATTN_OK) return st;
+  *cu_count = cus;
+  *clock_khz = khz;
+  return CPATTN_OK;
+}
+
 CPATTN_API const char* cpattn_status_string(cpattn_status s) {
   switch (s) {
     case CPATTN_OK: return "ok";

@@ -121,6 +121,13 @@ const char* cpattn_status_string(cpattn_status s);
  * calling thread ("" if none).  Valid until the next call on that thread. */
 const char* cpattn_last_hip_error(void);
 
+/* Compute units and peak shader clock (kHz) of HIP device `device`: the
+ * figures a dense matrix-core peak follows from (on gfx950, 4096 bf16 FLOP
+ * per clock per CU).  Host call, no launch.  CPATTN_ERR_INVALID_ARG for a
+ * NULL output or a negative device, CPATTN_ERR_HIP if HIP cannot query the
+ * device; the outputs are written only on success. */
+cpattn_status cpattn_device_info(int32_t device, int32_t* cu_count_host, int32_t* clock_khz_host);
+
 /* ---- zigzag partition -----------------------------------------------------
  * Zigzag split (LongVILA article, ZIGZAG-RINGATTN; the chunk rule is not
  * printed there, this is the reading that balances causal work exactly):

@@ -24,6 +24,15 @@ def test_exports_match_header(root_dir):
         assert hasattr(lib, name), name
 
 
+def test_device_info_rejects_bad_arguments():
+    # argument checks come before any HIP call, so this runs without a GPU
+    lib = c._lib
+    out = ctypes.c_int32(0)
+    assert lib.cpattn_device_info(0, None, ctypes.byref(out)) == c.ERR_INVALID_ARG
+    assert lib.cpattn_device_info(0, ctypes.byref(out), None) == c.ERR_INVALID_ARG
+    assert lib.cpattn_device_info(-1, ctypes.byref(out), ctypes.byref(out)) == c.ERR_INVALID_ARG
+
+
 def test_version_and_status_strings():
     assert "gfx950" in c.cpattn_version()
     assert c.status_string(c.OK) == "ok"

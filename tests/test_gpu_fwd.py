@@ -54,6 +54,12 @@ def test_partition_bitexact_and_roundtrip(cpa, dtype, lens, cp):
     assert torch.equal(back.cpu(), g.cpu())
 
 
+def test_device_info(cpa):
+    cus, khz = cpa.cpattn_device_info(0)
+    assert cus == torch.cuda.get_device_properties(0).multi_processor_count
+    assert 100_000 < khz < 10_000_000
+
+
 @pytest.mark.parametrize("dtype,heads,d", [("bf16", 28, 128), ("f32", 80, 128), ("bf16", 1, 64), ("f32", 7, 64)])
 def test_partition_rows_per_workgroup(cpa, dtype, heads, d):
     """Gather and scatter where a workgroup holds one row (80 fp32 heads: 2560
