@@ -13,10 +13,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // results over disjoint key sets combine as the softmax over their union:
 //   lse' = m + log(exp(lse - m) + exp(lse_p - m)),  m = max(lse, lse_p)
 //   out' = exp(lse - lse') out + exp(lse_p - lse') out_p
-// Rows are visited head-major (r = h*T + t) so LSE traffic is contiguous and
-// every (t, h) row of `out` is one contiguous run of d floats.  Each thread
-// owns 8 elements of a row; a row with lse_p = -inf is neither read nor
-// written (exact pass-through).
+// A row with lse_p = -inf is neither read nor written (exact pass-through).
+// (A variant keeping 4 rows in flight per thread, with a quarter of the
+// threads, measured slower: 72 -> 84 us per long-tail merge.)
 // ---------------------------------------------------------------------------
 
 
