@@ -78,7 +78,8 @@ def _load():
     # runtimes in one process do not share the device.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libcpattn.so not built at {LIB_PATH}; run python -m context_attention_varlen_amd.build")
+        raise ImportError(f"libcpattn.so not built at {LIB_PATH}; run python context_attention_varlen_amd/build.py "
+                          "(by path: importing the package needs the library)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     TP = ctypes.POINTER(Tensor)
