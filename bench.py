@@ -76,7 +76,7 @@ class Timer:
         out = {}
         for k, evs in self.events.items():
             ms = [a.elapsed_time(b) for a, b in evs]
-            out[k] = {"calls": len(ms), "total_ms": sum(ms), "avg_ms": sum(ms) / len(ms)}
+            out[k] = {"calls": len(ms), "total_ms": sum(ms), "avg_ms": sum(ms) / len(ms), "ms": ms}
         return out
 
 
@@ -454,8 +454,13 @@ def extras(c, torch):
         st = tm.stats()["fwd"]
         ms = st["total_ms"] / 3
         tfl = 4 * w.head_dim * w.heads_q * pairs / (ms * 1e-3) / 1e12
+        per_step = [sum(st["ms"][s::w.cp]) / 3 for s in range(w.cp)]
         out[name] = {"fwd_ms": round(ms, 3), "fwd_tflops": round(tfl, 1),
-                     "pct_peak": round(100 * tfl / PEAK_BF16_TFLOPS, 1), "pairs_per_head": pairs}
+                     "pct_peak": round(100 * tfl / PEAK_BF16_TFLOPS, 1), "pairs_per_head": pairs,
+                     "fwd_ms_per_ring_step": [round(x, 3) for x in per_step],
+                     "fwd_tflops_per_ring_step": [
+                         round(4 * w.head_dim * w.heads_q * c.cpattn_count_pairs(w.cu_seqlens, w.mask, sts[s])
+                               / (per_step[s] * 1e-3) / 1e12, 1) for s in range(w.cp)]}
         note(f"extra {name} forward done")
         if w.backward:
             do = partition(mk(w.heads_q), plan)
@@ -588,6 +593,11 @@ def main():
 
     per_call = {k: {"calls_per_step": v["calls"] // args.steps, "avg_ms": round(v["avg_ms"], 4),
                     "ms_per_step": round(v["total_ms"] / args.steps, 4)} for k, v in st.items()}
+    # ring step s of every timed step (step 0 holds the rank's own K/V share)
+    for k in ("fwd_step", "merge", "bwd_step"):
+        if k in st and per_call[k]["calls_per_step"] == w.cp:
+            ms = st[k]["ms"]
+            per_call[k]["per_ring_step_ms"] = [round(sum(ms[s::w.cp]) / len(ms[s::w.cp]), 4) for s in range(w.cp)]
     fwd_ms = st["fwd_step"]["total_ms"] / args.steps
     per_call["fwd_step"]["tflops"] = round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 1)
     if "bwd_step" in st:
