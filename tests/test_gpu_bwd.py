@@ -126,3 +126,28 @@ def test_backward_invariants_long_tail_scaled(cpa):
             scale = np.abs(do_loc).sum() / max(1, do_loc.size) * np.sqrt(do_loc.shape[0] * grp)
             assert np.max(np.abs(dv_sum[g] - want)) <= 2e-2 * max(1.0, scale)
             assert np.max(np.abs(dk_sum[g])) <= 2e-2 * max(1.0, scale)
+
+
+@pytest.mark.parametrize("bad", ["q", "k"])
+def test_bad_device_cu_seqlens_backward(cpa, bad):
+    """A non-monotone device cu_seqlens array (query or key side) schedules no
+    work in either list of the backward: the gradients are left as they were
+    and the workspace status reports INVALID_ARG; a valid call clears it."""
+    q = torch.randn(64, 4, 128, device="cuda").bfloat16()
+    kv = torch.randn(64, 2, 128, device="cuda").bfloat16()
+    do = torch.randn(64, 4, 128, device="cuda").bfloat16()
+    lse = torch.zeros(4, 64, device="cuda")
+    delta = torch.zeros(4, 64, device="cuda")
+    dq = torch.full((64, 4, 128), 7.0, device="cuda")
+    dk = torch.full((64, 2, 128), 7.0, device="cuda")
+    dv = torch.full((64, 2, 128), 7.0, device="cuda")
+    ws = torch.empty(cpa.cpattn_workspace_size(64, 64, 3), dtype=torch.uint8, device="cuda")
+    cu_ok = torch.tensor([0, 20, 40, 64], dtype=torch.int32, device="cuda")
+    cu_bad = torch.tensor([0, 40, 20, 64], dtype=torch.int32, device="cuda")
+    cu_q, cu_k = (cu_bad, cu_ok) if bad == "q" else (cu_ok, cu_bad)
+    st = cpa.make_step(1, 0, 0)
+    cpa.cpattn_bwd_step(q, kv, kv, do, lse, delta, cu_q, cu_k, 3, cpa.CAUSAL, st, 0.0, dq, dk, dv, ws)
+    assert cpa.cpattn_workspace_status(ws) == cpa.ERR_INVALID_ARG
+    assert torch.all(dq == 7.0) and torch.all(dk == 7.0) and torch.all(dv == 7.0)
+    cpa.cpattn_bwd_step(q, kv, kv, do, lse, delta, cu_ok, cu_ok, 3, cpa.CAUSAL, st, 0.0, dq, dk, dv, ws)
+    assert cpa.cpattn_workspace_status(ws) == cpa.OK
