@@ -24,6 +24,11 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kBins = 2048;
+// Per-sequence item offsets and per-item costs also stay in LDS when they
+// fit, so the binary search and the final scatter do not wait on global
+// memory written moments before; larger batches read them from the workspace.
+constexpr int kLdsSeqs = 2048;
+constexpr int kLdsItems = 8192;
 
 __device__ int block_excl_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63;
@@ -204,6 +209,8 @@ __device__ __forceinline__ void sched_body(const SchedArgs& a) {
   __shared__ int s_err;
   __shared__ int s_wave[kThreads / 64 + 1];
   __shared__ int s_bins[kBins];
+  __shared__ int s_seq_base[kLdsSeqs + 1];
+  __shared__ unsigned short s_bin_of[kLdsItems];
   const int tid = threadIdx.x;
   if (tid == 0) s_err = 0;
   for (int i = tid; i < kBins; i += kThreads) s_bins[i] = 0;
@@ -235,11 +242,15 @@ __device__ __forceinline__ void sched_body(const SchedArgs& a) {
     }
     int tot;
     const int ex = block_excl_scan(cnt, s_wave, &tot);
-    if (b < a.nseq) a.seq_base[b] = carry + ex;
+    if (b < a.nseq) {
+      a.seq_base[b] = carry + ex;
+      if (a.nseq <= kLdsSeqs) s_seq_base[b] = carry + ex;
+    }
     carry += tot;
   }
   if (tid == 0) {
     a.seq_base[a.nseq] = carry;
+    if (a.nseq <= kLdsSeqs) s_seq_base[a.nseq] = carry;
     if (carry > a.max_items) s_err = 1;
   }
   __syncthreads();
@@ -255,13 +266,14 @@ __device__ __forceinline__ void sched_body(const SchedArgs& a) {
   // ---- pass 2: build items -------------------------------------------------
   for (int idx = tid; idx < n_items; idx += kThreads) {
     // sequence: last b with seq_base[b] <= idx
+    const int* sb = a.nseq <= kLdsSeqs ? s_seq_base : a.seq_base;
     int lo = 0, hi = a.nseq - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (a.seq_base[mid] <= idx) lo = mid; else hi = mid - 1;
+      if (sb[mid] <= idx) lo = mid; else hi = mid - 1;
     }
     const int b = lo;
-    const int t_in_seq = idx - a.seq_base[b];
+    const int t_in_seq = idx - sb[b];
     const int pr0 = a.cu_p[b], lp = a.cu_p[b + 1] - pr0;
     const int sr0 = a.cu_s[b], ls = a.cu_s[b + 1] - sr0;
     if (a.mask == CPATTN_MASK_TF_BLOCK && cp > 1) {
@@ -275,6 +287,7 @@ __device__ __forceinline__ void sched_body(const SchedArgs& a) {
       it.cost = cost * a.cost_mult;
       a.items[idx] = it;
       atomicAdd(&s_bins[min(it.cost, kBins - 1)], 1);
+      if (idx < kLdsItems) s_bin_of[idx] = (unsigned short)min(it.cost, kBins - 1);
       continue;
     }
     const bool halves = cp > 1 && a.mask != CPATTN_MASK_BIDIR;
@@ -311,6 +324,7 @@ __device__ __forceinline__ void sched_body(const SchedArgs& a) {
     it.cost = cost * a.cost_mult;
     a.items[idx] = it;
     atomicAdd(&s_bins[min(it.cost, kBins - 1)], 1);
+    if (idx < kLdsItems) s_bin_of[idx] = (unsigned short)min(it.cost, kBins - 1);
   }
   __syncthreads();
 
@@ -328,7 +342,7 @@ __device__ __forceinline__ void sched_body(const SchedArgs& a) {
 
   // ---- pass 4: scatter ---------------------------------------------------------
   for (int idx = tid; idx < n_items; idx += kThreads) {
-    const int bin = min(a.items[idx].cost, kBins - 1);
+    const int bin = idx < kLdsItems ? (int)s_bin_of[idx] : min(a.items[idx].cost, kBins - 1);
     const int pos = atomicAdd(&s_bins[bin], 1);
     a.order[pos] = idx;
   }
