@@ -210,6 +210,7 @@ __device__ __forceinline__ void sched_body(const SchedArgs& a) {
   __shared__ int s_wave[kThreads / 64 + 1];
   __shared__ int s_bins[kBins];
   __shared__ int s_seq_base[kLdsSeqs + 1];
+  __shared__ int s_cu_p[kLdsSeqs + 1], s_cu_s[kLdsSeqs + 1];
   __shared__ unsigned short s_bin_of[kLdsItems];
   const int tid = threadIdx.x;
   if (tid == 0) s_err = 0;
@@ -225,6 +226,14 @@ __device__ __forceinline__ void sched_body(const SchedArgs& a) {
     if (b < a.nseq) {
       const int p0 = a.cu_p[b], p1 = a.cu_p[b + 1];
       const int s0 = a.cu_s[b], s1 = a.cu_s[b + 1];
+      if (a.nseq <= kLdsSeqs) {
+        s_cu_p[b + 1] = p1;
+        s_cu_s[b + 1] = s1;
+        if (b == 0) {
+          s_cu_p[0] = p0;
+          s_cu_s[0] = s0;
+        }
+      }
       bool bad = (b == 0 && (p0 != 0 || s0 != 0)) || p1 < p0 || s1 < s0 ||
                  (int64_t)p1 > a.tokens_p || (int64_t)s1 > a.tokens_s;
       const int lp = p1 - p0, ls = s1 - s0;
@@ -274,8 +283,10 @@ __device__ __forceinline__ void sched_body(const SchedArgs& a) {
     }
     const int b = lo;
     const int t_in_seq = idx - sb[b];
-    const int pr0 = a.cu_p[b], lp = a.cu_p[b + 1] - pr0;
-    const int sr0 = a.cu_s[b], ls = a.cu_s[b + 1] - sr0;
+    const int* cup = a.nseq <= kLdsSeqs ? s_cu_p : a.cu_p;
+    const int* cus = a.nseq <= kLdsSeqs ? s_cu_s : a.cu_s;
+    const int pr0 = cup[b], lp = cup[b + 1] - pr0;
+    const int sr0 = cus[b], ls = cus[b + 1] - sr0;
     if (a.mask == CPATTN_MASK_TF_BLOCK && cp > 1) {
       WorkItem it;
       it.seq = b;
