@@ -56,7 +56,7 @@ def _draw(seed):
     return lens, cp, rank, hq, hkv, d, mode, (0, 0)
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(160))
 def test_random_shape(cpa, seed):
     lens, cp, r, hq, hkv, d, mode, tf = _draw(seed)
     print(f"seed {seed}: lens {lens} cp {cp} rank {r} heads {hq}/{hkv} d {d} mode {mode} tf {tf}", flush=True)
@@ -77,7 +77,7 @@ def test_random_shape(cpa, seed):
         _check_grad(dv[j], dv_r[j], f"dv[{j}]")
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(16))
 def test_random_shape_f32(cpa, seed):
     """The fp32 path on the same kind of draws (fp32 inputs, no bf16
     anywhere), to its tolerance."""
@@ -105,7 +105,7 @@ def test_random_shape_f32(cpa, seed):
         _check_grad(dv[j], dv_r[j], f"dv[{j}]", tol=1e-4)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(16))
 def test_random_balanced_tf_split(cpa, seed):
     """Teacher forcing at cp > 1 under the balanced split: random B >= 32,
     N a multiple of cp (a partial last dealing round included), every rank's
