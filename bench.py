@@ -201,9 +201,8 @@ def run_hot_path(c, torch, w, steps, warmup, graph=True):
                 bufs.out_partial, bufs.lse_partial, bufs.workspace))
             tm("merge", lambda: c.cpattn_merge(bufs.out, bufs.lse, bufs.out_partial, bufs.lse_partial))
         if w.backward:
-            dq.zero_()
-            for t_ in dk + dv:
-                t_.zero_()
+            for t_ in [dq] + dk + dv:
+                c.cpattn_fill_f32(t_, 0.0)
             tm("bwd_preprocess", lambda: c.cpattn_bwd_preprocess(bufs.out, do, delta))
             for s in range(w.cp):
                 j = (r - s) % w.cp

@@ -30,7 +30,7 @@ EXPORTS = (
     "cpattn_seq_to_head", "cpattn_head_to_seq", "cpattn_split_hw", "cpattn_partition_index_hw",
     "cpattn_partition_hw", "cpattn_unpartition_hw",
     "cpattn_count_pairs", "cpattn_workspace_size", "cpattn_workspace_status",
-    "cpattn_fwd_step", "cpattn_merge", "cpattn_bwd_preprocess", "cpattn_bwd_step",
+    "cpattn_fwd_step", "cpattn_merge", "cpattn_fill_f32", "cpattn_bwd_preprocess", "cpattn_bwd_step",
     "cpattn_dcp_plan_batch", "cpattn_dcp_quotas",
 )
 
@@ -106,6 +106,7 @@ def _load():
         "cpattn_workspace_status": (ctypes.c_int, [P, P, ctypes.POINTER(ctypes.c_int)]),
         "cpattn_fwd_step": (ctypes.c_int, [TP, TP, TP, P, P, I32, ctypes.c_int, SP, F, TP, P, P, S, P]),
         "cpattn_merge": (ctypes.c_int, [P, P, TP, P, P]),
+        "cpattn_fill_f32": (ctypes.c_int, [P, I64, F, P]),
         "cpattn_bwd_preprocess": (ctypes.c_int, [P, TP, P, P]),
         "cpattn_bwd_step": (ctypes.c_int, [TP, TP, TP, TP, P, P, P, P, I32, ctypes.c_int, SP, F,
                                            P, P, P, P, S, P]),
@@ -318,6 +319,14 @@ def cpattn_merge(out, lse, out_partial, lse_partial, stream=None):
     st = _lib.cpattn_merge(_ptr(out), _ptr(lse), ctypes.byref(_tensor(out_partial)), _ptr(lse_partial),
                            _stream(stream))
     _check(st, "cpattn_merge")
+
+
+def cpattn_fill_f32(t, value: float, stream=None):
+    """Every element of the contiguous fp32 tensor t set to value (library kernel)."""
+    import torch
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise CpattnError(ERR_INVALID_ARG, "cpattn_fill_f32")
+    _check(_lib.cpattn_fill_f32(_ptr(t), t.numel(), float(value), _stream(stream)), "cpattn_fill_f32")
 
 
 def cpattn_bwd_preprocess(out, dout, delta, stream=None):

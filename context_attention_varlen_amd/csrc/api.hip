@@ -531,6 +531,13 @@ CPATTN_API cpattn_status cpattn_merge(float* out, float* lse, const cpattn_tenso
   return hip_status(launch_merge(a, (hipStream_t)stream));
 }
 
+CPATTN_API cpattn_status cpattn_fill_f32(float* dst, int64_t count, float value, void* stream) {
+  if (count < 0 || (count > 0 && (!dst || !aligned16(dst)))) return CPATTN_ERR_INVALID_ARG;
+  if (count == 0) return CPATTN_OK;
+  clear_stale_error();
+  return hip_status(launch_fill(dst, count, value, (hipStream_t)stream));
+}
+
 CPATTN_API cpattn_status cpattn_bwd_preprocess(const float* out, const cpattn_tensor* dout, float* delta,
                                                void* stream) {
   cpattn_status st;

@@ -220,6 +220,7 @@ int bwd_dq_tile_rows(bool bf16);
 int bwd_dkv_tile_rows(bool bf16);
 hipError_t launch_bwd(BwdArgs a, bool bf16, int d, int64_t max_items_q, int64_t max_items_k, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_fill(float* dst, int64_t count, float value, hipStream_t stream);
 hipError_t launch_delta(const DeltaArgs& a, hipStream_t stream);
 hipError_t launch_partition(PartArgs a, hipStream_t stream);
 

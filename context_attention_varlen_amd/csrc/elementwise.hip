@@ -94,6 +94,26 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
+// Fill: the ring's starting state (out = 0, lse = -inf, the merge identity)
+// and zeroed gradient accumulators.  One thread stores 16 bytes,
+// nontemporal (every byte is written once and not read back soon); the
+// last count mod 4 values are stored singly by the first threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fill_kernel(float* dst, int64_t count, float value) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nvec = count >> 2;
+  if (i < nvec) st_nt(f32x4{value, value, value, value}, (f32x4*)dst + i);
+  const int64_t tail = count - (nvec << 2);
+  if (i < tail) dst[(nvec << 2) + i] = value;
+}
+
+hipError_t launch_fill(float* dst, int64_t count, float value, hipStream_t stream) {
+  const int64_t threads = std::max<int64_t>(count >> 2, 3);
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, dst, count, value);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Backward preprocess: delta[h][t] = <dO[t,h,:], O[t,h,:]>.
 // ---------------------------------------------------------------------------
 

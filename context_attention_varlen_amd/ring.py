@@ -16,7 +16,7 @@ from typing import List, Optional
 import numpy as np
 import torch
 
-from . import (cpattn_bwd_preprocess, cpattn_bwd_step, cpattn_fwd_step, cpattn_merge,
+from . import (cpattn_bwd_preprocess, cpattn_bwd_step, cpattn_fill_f32, cpattn_fwd_step, cpattn_merge,
                cpattn_partition, cpattn_partition_index, cpattn_partition_index_tf, cpattn_partition_tf,
                cpattn_workspace_size, make_step)
 
@@ -80,8 +80,9 @@ class ForwardBuffers:
                               torch.empty((hq, t), dtype=torch.float32, device=dev), ws)
 
     def reset(self):
-        self.out.zero_()
-        self.lse.fill_(-float("inf"))
+        """The ring's starting state, out = 0 and lse = -inf (library fill kernel)."""
+        cpattn_fill_f32(self.out, 0.0)
+        cpattn_fill_f32(self.lse, -float("inf"))
 
 
 def ring_forward(q_local: torch.Tensor, k_shares: List[torch.Tensor], v_shares: List[torch.Tensor],
@@ -120,9 +121,8 @@ def ring_backward(q_local, k_shares, v_shares, dout_local, bufs: ForwardBuffers,
         delta = torch.empty((hq, t), dtype=torch.float32, device=dev)
     else:
         dq, dk, dv, delta = grads
-        dq.zero_()
-        for x in dk + dv:
-            x.zero_()
+        for x in [dq] + dk + dv:
+            cpattn_fill_f32(x, 0.0)
     cpattn_bwd_preprocess(bufs.out, dout_local, delta)
     for s in range(plan.cp):
         j = (plan.rank - s) % plan.cp

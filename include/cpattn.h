@@ -291,6 +291,14 @@ cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_tensor* k, co
 cpattn_status cpattn_merge(float* out_dev, float* lse_dev, const cpattn_tensor* out_partial,
                            const float* lse_partial_dev, void* stream);
 
+/* Sets count fp32 values at dst_dev to `value`: the ring's starting state
+ * before the first merge (running out = 0, running lse = -inf: the merge of
+ * a result over no keys) and the zeroed gradient accumulators that
+ * cpattn_bwd_step adds into.  dst_dev 16-byte aligned; count 0 enqueues
+ * nothing.  A kernel, not a memset, so it records into HIP graphs like the
+ * other calls.  INVALID_ARG for a NULL or misaligned pointer or count < 0. */
+cpattn_status cpattn_fill_f32(float* dst_dev, int64_t count, float value, void* stream);
+
 /* ---- backward --------------------------------------------------------------
  * delta_dev[h][t] = <dout[t,h,:], out[t,h,:]> with out the final merged fp32
  * output (dense [T][H][d]).  dout: [T, H, d] bf16 or fp32 view. */

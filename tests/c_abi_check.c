@@ -46,6 +46,8 @@ int main(void) {
     CHECK(sh * sw == 8 && 30 % sh == 0 && 52 % sw == 0);
   }
   CHECK(cpattn_workspace_size(64, 64, 1) > 0);
+  CHECK(cpattn_fill_f32(NULL, 0, 0.0f, NULL) == CPATTN_OK);
+  CHECK(cpattn_fill_f32(NULL, 4, 0.0f, NULL) == CPATTN_ERR_INVALID_ARG);
   printf("c abi ok\n");
   return 0;
 }

@@ -17,7 +17,7 @@ c = pytest.importorskip("context_attention_varlen_amd")
 
 def test_exports_match_header(root_dir):
     hdr = open(os.path.join(root_dir, "include", "cpattn.h")).read()
-    declared = set(re.findall(r"\b(cpattn_[a-z_]+)\s*\(", hdr))
+    declared = set(re.findall(r"\b(cpattn_[a-z0-9_]+)\s*\(", hdr))
     assert declared == set(c.EXPORTS)
     lib = ctypes.CDLL(c.LIB_PATH)
     for name in declared:
@@ -31,6 +31,15 @@ def test_device_info_rejects_bad_arguments():
     assert lib.cpattn_device_info(0, None, ctypes.byref(out)) == c.ERR_INVALID_ARG
     assert lib.cpattn_device_info(0, ctypes.byref(out), None) == c.ERR_INVALID_ARG
     assert lib.cpattn_device_info(-1, ctypes.byref(out), ctypes.byref(out)) == c.ERR_INVALID_ARG
+
+
+def test_fill_rejects_bad_arguments():
+    # checked before any launch; count 0 enqueues nothing
+    lib = c._lib
+    assert lib.cpattn_fill_f32(None, 4, ctypes.c_float(0.0), None) == c.ERR_INVALID_ARG
+    assert lib.cpattn_fill_f32(ctypes.c_void_p(16), -1, ctypes.c_float(0.0), None) == c.ERR_INVALID_ARG
+    assert lib.cpattn_fill_f32(ctypes.c_void_p(20), 4, ctypes.c_float(0.0), None) == c.ERR_INVALID_ARG
+    assert lib.cpattn_fill_f32(None, 0, ctypes.c_float(0.0), None) == c.OK
 
 
 def test_version_and_status_strings():

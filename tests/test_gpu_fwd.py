@@ -54,6 +54,19 @@ def test_partition_bitexact_and_roundtrip(cpa, dtype, lens, cp):
     assert torch.equal(back.cpu(), g.cpu())
 
 
+@pytest.mark.parametrize("count", [0, 1, 3, 4, 5, 1023, (1 << 20) + 3])
+def test_fill_f32(cpa, count):
+    """Exact fill of count values (16-byte stores plus a ragged tail), the
+    ring's -inf and 0 included; nothing past count is written."""
+    for value in (0.0, -float("inf"), 1.5):
+        buf = torch.full((count + 64,), 7.0, device="cuda")
+        cpa.cpattn_fill_f32(buf[:count], value)
+        torch.cuda.synchronize()
+        head, rest = buf[:count].cpu(), buf[count:].cpu()
+        assert torch.equal(head, torch.full((count,), value))
+        assert torch.all(rest == 7.0)
+
+
 def test_device_info(cpa):
     cus, khz = cpa.cpattn_device_info(0)
     assert cus == torch.cuda.get_device_properties(0).multi_processor_count
