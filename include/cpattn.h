@@ -18,11 +18,12 @@
  *
  * Calling sequence for rank r of cp ranks:
  *     cpattn_partition (Q to rank r, K/V to every source rank)
- *     out = 0, lse = -inf
+ *     out = 0, lse = -inf                        (cpattn_fill_f32)
  *     for s in 0..cp-1:
  *         cpattn_fwd_step(step = {cp, r, s})     -> out_partial, lse_partial
  *         cpattn_merge(out, lse, out_partial, lse_partial)
  *     backward:
+ *         dq, dk, dv = 0                         (cpattn_fill_f32)
  *         cpattn_bwd_preprocess(out, dout)       -> delta
  *         for s in 0..cp-1: cpattn_bwd_step(step = {cp, r, s})
  *
