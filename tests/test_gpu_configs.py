@@ -111,6 +111,37 @@ def test_long_video_rank(cpa, long_video_inputs, rank):
         == 4_294_983_680
 
 
+@pytest.fixture(scope="module")
+def two_million():
+    """One 2,097,152-token sequence (the >2M-token contexts of the long-video
+    pages), zigzag cp = 8, GQA 2/1, d = 128, bf16 0.5 N(0,1)."""
+    w = workloads.Workload("two_million_tokens", (1 << 21,), heads_q=2, heads_kv=1, head_dim=128, dtype="bf16",
+                           mask=oracle.CAUSAL, cp=8, rank=0, value_scale=0.5, seed=7)
+    return w, workloads.draw(w)
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_two_million_token_sequence(cpa, two_million, rank):
+    """The largest shape in the suite: positions up to 2^21 and 262144 local
+    rows per rank; all 8 forward steps and merges, sampled merged rows and
+    step partials against the oracle, and the exact per-rank pair count."""
+    w, x = two_million
+    plan, bufs, parts, _ = _gpu_ring(w, x, rank, keep=True)
+    rows = _sample_local_rows(w, rank, 12, 0)
+    o_ref, l_ref = _oracle_rows(w, x, rank, rows)
+    t = torch.from_numpy(rows).cuda()
+    check_out(bufs.out[t].cpu().numpy(), o_ref, "bf16")
+    check_lse(bufs.lse[:, t].cpu().numpy(), l_ref)
+    for s in (0, 5):
+        o_ref, l_ref = _oracle_rows(w, x, rank, rows, step=s)
+        op, lp = parts[s]
+        check_out(op[t].float().cpu().numpy(), o_ref, "bf16")
+        check_lse(lp[:, t].cpu().numpy(), l_ref)
+    L = 1 << 21
+    assert sum(cpa.cpattn_count_pairs(w.cu_seqlens, w.mask, cpa.make_step(8, rank, s)) for s in range(8)) \
+        == L * L // 16 + L // 16
+
+
 def test_tf_dit_sampled(cpa):
     """Teacher-forced DiT, 74880 tokens, block mask: sampled rows stratified
     over both streams and the chunk edges (B = 3120 is not a tile multiple)."""
