@@ -590,6 +590,17 @@ def main():
                 "traffic": traffic_for(kname), "avg_launch_ms": round(avg_ms, 4),
                 "algorithmic_flops_per_launch": int(flops_per_launch)}
 
+    # the other attention kernel of the step, on the same footing (not the dominant one)
+    other = [k for k in kern if k in st and k != dom]
+    roofline_other = None
+    if other:
+        k2 = other[0]
+        n2, f2 = kern[k2]
+        a2 = f2 / (st[k2]["avg_ms"] * 1e-3) / 1e12
+        roofline_other = {"bound": "mfma", "kernel": n2, "achieved": round(a2, 1), "peak": PEAK_BF16_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(a2 / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(n2),
+                          "avg_launch_ms": round(st[k2]["avg_ms"], 4), "algorithmic_flops_per_launch": int(f2)}
+
     per_call = {k: {"calls_per_step": v["calls"] // args.steps, "avg_ms": round(v["avg_ms"], 4),
                     "ms_per_step": round(v["total_ms"] / args.steps, 4)} for k, v in st.items()}
     # ring step s of every timed step (step 0 holds the rank's own K/V share)
@@ -617,7 +628,7 @@ def main():
                    "global_batch": 1, "seq_len": w.tokens, "tokens_local": w.tokens // w.cp,
                    "parallelism": f"cp{w.cp} (one rank's share on one GPU)"},
         "pairs_per_head": P, "flops_per_step": fwd_flops + bwd_flops, "outputs_finite": finite,
-        "per_call": per_call, "roofline": roofline,
+        "per_call": per_call, "roofline": roofline, "roofline_other_attention_kernel": roofline_other,
         # not `value`: the same step captured once as a HIP graph and replayed
         # `steps` times after the timed region (no per-call launch gaps)
         "graph_replay": None if graph_ms is None else {
