@@ -13,7 +13,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // results over disjoint key sets combine as the softmax over their union:
 //   lse' = m + log(exp(lse - m) + exp(lse_p - m)),  m = max(lse, lse_p)
 //   out' = exp(lse - lse') out + exp(lse_p - lse') out_p
-// A row with lse_p = -inf is neither read nor written (exact pass-through).
+// A row with lse_p = -inf passes through (out is neither read nor written),
+// except that a row whose running lse is still -inf is set to 0 (the result
+// over no keys): the running output needs no initialisation.
 // (A variant keeping 4 rows in flight per thread, with a quarter of the
 // threads, measured slower: 72 -> 84 us per long-tail merge.)
 // ---------------------------------------------------------------------------
@@ -54,9 +56,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int h = (int)(r - t * a.heads);
   const int64_t li = (int64_t)h * a.tokens + t;
   const float lp = a.lsep[li];
-  if (lp == -INFINITY) return;
   const float lo = a.lse[li];
   float* o = a.out + r * D + 4 * c;
+  if (lp == -INFINITY) {
+    // nothing to add; a row not yet merged (running lse -inf) becomes the
+    // result over no keys, 0, so the running output needs no initialisation
+    if (lo == -INFINITY) st_nt(f32x4{0.f, 0.f, 0.f, 0.f}, (f32x4*)o);
+    return;
+  }
   const void* prow = (const char*)a.op + (t * a.op_st + (int64_t)h * a.op_sh) * (BF16 ? 2 : 4);
   const f32x4 p = load4<BF16>(prow, 4 * c);
   f32x4 v;

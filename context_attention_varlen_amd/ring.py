@@ -80,8 +80,8 @@ class ForwardBuffers:
                               torch.empty((hq, t), dtype=torch.float32, device=dev), ws)
 
     def reset(self):
-        """The ring's starting state, out = 0 and lse = -inf (library fill kernel)."""
-        cpattn_fill_f32(self.out, 0.0)
+        """The ring's starting state, lse = -inf (library fill kernel); the merge
+        writes every running row whose lse is -inf, so out needs no fill."""
         cpattn_fill_f32(self.lse, -float("inf"))
 
 

@@ -18,7 +18,7 @@
  *
  * Calling sequence for rank r of cp ranks:
  *     cpattn_partition (Q to rank r, K/V to every source rank)
- *     out = 0, lse = -inf                        (cpattn_fill_f32)
+ *     lse = -inf (out needs no initialisation)   (cpattn_fill_f32)
  *     for s in 0..cp-1:
  *         cpattn_fwd_step(step = {cp, r, s})     -> out_partial, lse_partial
  *         cpattn_merge(out, lse, out_partial, lse_partial)
@@ -284,7 +284,8 @@ cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_tensor* k, co
  *     lse' = log(exp(lse) + exp(lse_p))
  *     out' = exp(lse - lse') * out + exp(lse_p - lse') * out_p
  * Rows with lse_p = -inf pass through bit-exact (and are not read);
- * running rows at -inf take the partial.
+ * running rows at -inf take the partial, or 0 when lse_p is -inf too, so
+ * out_dev needs no initialisation: the starting state is lse = -inf.
  *   out_dev      fp32 [T][H][d] dense, running output (in/out)
  *   lse_dev      fp32 [H][T], running LSE (in/out)
  *   out_partial  [T, H, d] bf16 or fp32 view
@@ -293,9 +294,8 @@ cpattn_status cpattn_merge(float* out_dev, float* lse_dev, const cpattn_tensor* 
                            const float* lse_partial_dev, void* stream);
 
 /* Sets count fp32 values at dst_dev to `value`: the ring's starting state
- * before the first merge (running out = 0, running lse = -inf: the merge of
- * a result over no keys) and the zeroed gradient accumulators that
- * cpattn_bwd_step adds into.  dst_dev 16-byte aligned; count 0 enqueues
+ * before the first merge (running lse = -inf: a result over no keys) and the
+ * zeroed gradient accumulators that cpattn_bwd_step adds into.  dst_dev 16-byte aligned; count 0 enqueues
  * nothing.  A kernel, not a memset, so it records into HIP graphs like the
  * other calls.  INVALID_ARG for a NULL or misaligned pointer or count < 0. */
 cpattn_status cpattn_fill_f32(float* dst_dev, int64_t count, float value, void* stream);

@@ -204,6 +204,9 @@ def test_merge_passthrough_bit_exact(cpa):
     lp = torch.full((H, T), -float("inf"), device="cuda")
     cpa.cpattn_merge(out, lse, part, lp)
     torch.cuda.synchronize()
+    # finite running rows pass through bit-exact; rows never merged (running
+    # lse -inf) become the result over no keys, 0
+    o0[5:50, 1, :] = 0.0
     assert torch.equal(out, o0) and torch.equal(lse, l0)
     # running rows at -inf take the partial exactly
     lp2 = torch.randn(H, T, device="cuda")
@@ -212,6 +215,24 @@ def test_merge_passthrough_bit_exact(cpa):
     cpa.cpattn_merge(out, lse, part, lp2)
     torch.cuda.synchronize()
     assert torch.equal(out.permute(1, 0, 2), part.float().permute(1, 0, 2)) and torch.equal(lse, lp2)
+
+
+def test_merge_first_needs_no_output_init(cpa):
+    """From the starting state lse = -inf the running output's old contents
+    do not matter: rows with a finite partial LSE take the partial exactly,
+    rows whose partial is -inf too become 0 (the result over no keys)."""
+    T, H, d = 300, 3, 128
+    out = torch.full((T, H, d), float("nan"), device="cuda")
+    lse = torch.full((H, T), -float("inf"), device="cuda")
+    part = torch.randn(T, H, d, device="cuda").bfloat16()
+    lp = torch.randn(H, T, device="cuda")
+    lp[0, 7:90] = -float("inf")
+    lp[2, 250:] = -float("inf")
+    cpa.cpattn_merge(out, lse, part, lp)
+    torch.cuda.synchronize()
+    live = torch.isfinite(lp).t()                    # [T, H]
+    ref = torch.where(live[..., None], part.float(), torch.zeros_like(out))
+    assert torch.equal(out, ref) and torch.equal(lse, lp)
 
 
 def test_merge_against_oracle(cpa):
