@@ -9,7 +9,7 @@ pytestmark = pytest.mark.gpu
 
 import oracle  # noqa: E402
 import workloads  # noqa: E402
-from tests._gpu import TOL_GRAD_RELRMS, dev, rel_rms, tdtype  # noqa: E402
+from tests._gpu import TOL_GRAD_RELRMS, check_lse, check_out, dev, rel_rms, tdtype  # noqa: E402
 
 
 @pytest.fixture(scope="module")
@@ -151,3 +151,29 @@ def test_bad_device_cu_seqlens_backward(cpa, bad):
     assert torch.all(dq == 7.0) and torch.all(dk == 7.0) and torch.all(dv == 7.0)
     cpa.cpattn_bwd_step(q, kv, kv, do, lse, delta, cu_ok, cu_ok, 3, cpa.CAUSAL, st, 0.0, dq, dk, dv, ws)
     assert cpa.cpattn_workspace_status(ws) == cpa.OK
+
+
+def test_many_sequences_global_schedule_path(cpa):
+    """Over 2048 sequences and over 8192 work items per tile list: the
+    scheduler keeps per-sequence offsets, cu_seqlens and item cost bins in
+    workspace memory instead of LDS.  5000 short sequences (some empty) at
+    cp = 2, forward and backward of rank 1 against the oracle."""
+    rng = np.random.default_rng(77)
+    lens = [int(4 * rng.integers(1, 11)) for _ in range(5000)]
+    for i in rng.choice(5000, size=40, replace=False):
+        lens[int(i)] = 0
+    assert len(lens) > 2048 and 2 * sum(1 for L in lens if L) > 8192
+    x, cu = _inputs(78, lens, 2, 1, 64, "bf16")
+    mode = oracle.CAUSAL
+    dq, dk, dv, delta, bufs = run_gpu(x, cu, 2, 1, mode, "bf16")
+    _, l2g, qpos, qseq = oracle.local_rows(cu, 2, 1)
+    seq = np.repeat(np.arange(len(cu) - 1), np.diff(cu))
+    pos = np.arange(int(cu[-1])) - cu[seq]
+    o_ref, l_ref = oracle.attention(x["q"][l2g], x["k"], x["v"], qseq, qpos, seq, pos, mode)
+    check_out(bufs.out.cpu().numpy(), o_ref, "bf16")
+    check_lse(bufs.lse.cpu().numpy(), l_ref)
+    dq_r, dk_r, dv_r, _ = oracle_grads(x, cu, 2, 1, mode)
+    _check_grad(dq, dq_r, "dq")
+    for j in range(2):
+        _check_grad(dk[j], dk_r[j], f"dk[{j}]")
+        _check_grad(dv[j], dv_r[j], f"dv[{j}]")
