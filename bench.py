@@ -195,7 +195,7 @@ def run_hot_path(c, torch, w, steps, warmup, graph=True):
             tm("partition", lambda j=j: c.cpattn_partition(g["v"], vs[j], cu_g, nseq, w.cp, j))
         bufs.reset()
         for s in range(w.cp):
-            j = (r - s) % w.cp
+            j = c.cpattn_step_source(steps_[s])
             tm("fwd_step", lambda s=s, j=j: c.cpattn_fwd_step(
                 q, ks[j], vs[j], plan.cu_local_dev, plan.cu_local_dev, nseq, w.mask, steps_[s], 0.0,
                 bufs.out_partial, bufs.lse_partial, bufs.workspace))
@@ -205,7 +205,7 @@ def run_hot_path(c, torch, w, steps, warmup, graph=True):
                 c.cpattn_fill_f32(t_, 0.0)
             tm("bwd_preprocess", lambda: c.cpattn_bwd_preprocess(bufs.out, do, delta))
             for s in range(w.cp):
-                j = (r - s) % w.cp
+                j = c.cpattn_step_source(steps_[s])
                 tm("bwd_step", lambda s=s, j=j: c.cpattn_bwd_step(
                     q, ks[j], vs[j], do, bufs.lse, delta, plan.cu_local_dev, plan.cu_local_dev, nseq, w.mask,
                     steps_[s], 0.0, dq, dk[j], dv[j], bufs.workspace))
@@ -223,6 +223,10 @@ def run_hot_path(c, torch, w, steps, warmup, graph=True):
         marks[i + 1].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # a schedule the device rejected (bad cu_seqlens) would time empty kernels
+    ws_status = c.cpattn_workspace_status(bufs.workspace)
+    if ws_status != c.OK:
+        raise SystemExit(f"bench: the tile scheduler rejected the batch: {c.status_string(ws_status)}")
     step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
     spread = {"median": round(step_ms[steps // 2] if steps % 2 else (step_ms[steps // 2 - 1] + step_ms[steps // 2]) / 2, 4),
               "min": round(step_ms[0], 4), "max": round(step_ms[-1], 4)}
@@ -443,7 +447,7 @@ def extras(c, torch):
         for it in range(4):
             bufs.reset()
             for s in range(w.cp):
-                j = (w.rank - s) % w.cp
+                j = c.cpattn_step_source(sts[s])
                 f = lambda s=s, j=j: c.cpattn_fwd_step(q, ks[j], vs[j], plan.cu_local_dev, plan.cu_local_dev,  # noqa
                                                        plan.num_seqs, w.mask, sts[s], 0.0, bufs.out_partial,
                                                        bufs.lse_partial, bufs.workspace)
@@ -471,7 +475,7 @@ def extras(c, torch):
             for it in range(4):
                 c.cpattn_bwd_preprocess(bufs.out, do, delta)
                 for s in range(w.cp):
-                    j = (w.rank - s) % w.cp
+                    j = c.cpattn_step_source(sts[s])
                     f = lambda s=s, j=j: c.cpattn_bwd_step(q, ks[j], vs[j], do, bufs.lse, delta,  # noqa: E731
                                                            plan.cu_local_dev, plan.cu_local_dev, plan.num_seqs,
                                                            w.mask, sts[s], 0.0, dq, dk, dv, bufs.workspace)

@@ -22,14 +22,14 @@ LIB_PATH = os.path.join(_HERE, "libcpattn.so")
 
 CAUSAL, BIDIR, TF_BLOCK = 0, 1, 2
 F32, BF16 = 0, 1
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_INFEASIBLE = 0, 1, 2, 3, 4, 5
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_INFEASIBLE, ERR_NOMEM = 0, 1, 2, 3, 4, 5, 6
 
 EXPORTS = (
     "cpattn_version", "cpattn_status_string", "cpattn_last_hip_error", "cpattn_device_info", "cpattn_partition_index", "cpattn_partition",
     "cpattn_unpartition", "cpattn_partition_index_tf", "cpattn_partition_tf", "cpattn_unpartition_tf",
     "cpattn_seq_to_head", "cpattn_head_to_seq", "cpattn_split_hw", "cpattn_partition_index_hw",
     "cpattn_partition_hw", "cpattn_unpartition_hw",
-    "cpattn_count_pairs", "cpattn_workspace_size", "cpattn_workspace_status",
+    "cpattn_count_pairs", "cpattn_step_source", "cpattn_workspace_size", "cpattn_workspace_status",
     "cpattn_fwd_step", "cpattn_merge", "cpattn_fill_f32", "cpattn_bwd_preprocess", "cpattn_bwd_step",
     "cpattn_dcp_plan_batch", "cpattn_dcp_quotas",
 )
@@ -102,6 +102,7 @@ def _load():
         "cpattn_unpartition_hw": (ctypes.c_int, [TP, TP, P, I32, I32, I32, I32, I32, I32, I32, P]),
         "cpattn_head_to_seq": (ctypes.c_int, [TP, I32, I32, TP, P]),
         "cpattn_count_pairs": (I64, [P, I32, ctypes.c_int, SP]),
+        "cpattn_step_source": (I32, [SP]),
         "cpattn_workspace_size": (S, [I64, I64, I32]),
         "cpattn_workspace_status": (ctypes.c_int, [P, P, ctypes.POINTER(ctypes.c_int)]),
         "cpattn_fwd_step": (ctypes.c_int, [TP, TP, TP, P, P, I32, ctypes.c_int, SP, F, TP, P, P, S, P]),
@@ -149,11 +150,49 @@ def _tensor(t) -> Tensor:
         raise ValueError("THD tensors are [tokens, heads, head_dim]")
     if t.stride(2) != 1:
         raise ValueError("head_dim must be contiguous")
+    if not t.is_cuda:
+        raise ValueError("THD tensors must be in device memory")
     return Tensor(t.data_ptr(), _dtype_code(t), t.shape[0], t.shape[1], t.shape[2], t.stride(0), t.stride(1))
 
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# The C ABI takes raw pointers for these arrays; what their declarations in
+# cpattn.h require is checked here so that a wrong torch dtype, device, shape
+# or layout raises instead of reaching the device.
+def _dev_array(t, name, dtype, shape):
+    import torch
+    if t is None:
+        raise ValueError(f"{name}: missing")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be in device memory")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    del torch
+
+
+def _cu(t, name, num_seqs):
+    import torch
+    _dev_array(t, name, torch.int32, (num_seqs + 1,))
+    return _ptr(t)
+
+
+def _f32(t, name, shape):
+    import torch
+    _dev_array(t, name, torch.float32, shape)
+    return _ptr(t)
+
+
+def _workspace(t):
+    if t is None or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("workspace: a contiguous device tensor")
+    return _ptr(t), t.numel() * t.element_size()
 
 
 def _stream(stream):
@@ -195,13 +234,13 @@ def cpattn_partition_index(cu_seqlens_global, cp: int, rank: int, with_map: bool
 
 def cpattn_partition(src_global, dst_local, cu_seqlens_global_dev, num_seqs, cp, rank, stream=None):
     st = _lib.cpattn_partition(ctypes.byref(_tensor(src_global)), ctypes.byref(_tensor(dst_local)),
-                               _ptr(cu_seqlens_global_dev), num_seqs, cp, rank, _stream(stream))
+                               _cu(cu_seqlens_global_dev, "cu_seqlens_global", num_seqs), num_seqs, cp, rank, _stream(stream))
     _check(st, "cpattn_partition")
 
 
 def cpattn_unpartition(src_local, dst_global, cu_seqlens_global_dev, num_seqs, cp, rank, stream=None):
     st = _lib.cpattn_unpartition(ctypes.byref(_tensor(src_local)), ctypes.byref(_tensor(dst_global)),
-                                 _ptr(cu_seqlens_global_dev), num_seqs, cp, rank, _stream(stream))
+                                 _cu(cu_seqlens_global_dev, "cu_seqlens_global", num_seqs), num_seqs, cp, rank, _stream(stream))
     _check(st, "cpattn_unpartition")
 
 
@@ -222,7 +261,7 @@ def cpattn_partition_index_tf(cu_seqlens_global, cp: int, rank: int, tf_chunk_to
 def cpattn_partition_tf(src_global, dst_local, cu_seqlens_global_dev, num_seqs, cp, rank, tf_chunk_tokens,
                         tf_num_chunks, stream=None):
     st = _lib.cpattn_partition_tf(ctypes.byref(_tensor(src_global)), ctypes.byref(_tensor(dst_local)),
-                                  _ptr(cu_seqlens_global_dev), num_seqs, cp, rank, tf_chunk_tokens, tf_num_chunks,
+                                  _cu(cu_seqlens_global_dev, "cu_seqlens_global", num_seqs), num_seqs, cp, rank, tf_chunk_tokens, tf_num_chunks,
                                   _stream(stream))
     _check(st, "cpattn_partition_tf")
 
@@ -230,7 +269,7 @@ def cpattn_partition_tf(src_global, dst_local, cu_seqlens_global_dev, num_seqs, 
 def cpattn_unpartition_tf(src_local, dst_global, cu_seqlens_global_dev, num_seqs, cp, rank, tf_chunk_tokens,
                           tf_num_chunks, stream=None):
     st = _lib.cpattn_unpartition_tf(ctypes.byref(_tensor(src_local)), ctypes.byref(_tensor(dst_global)),
-                                    _ptr(cu_seqlens_global_dev), num_seqs, cp, rank, tf_chunk_tokens, tf_num_chunks,
+                                    _cu(cu_seqlens_global_dev, "cu_seqlens_global", num_seqs), num_seqs, cp, rank, tf_chunk_tokens, tf_num_chunks,
                                     _stream(stream))
     _check(st, "cpattn_unpartition_tf")
 
@@ -258,7 +297,7 @@ def cpattn_partition_index_hw(cu_seqlens_global, frames, H, W, split, rank, with
 def cpattn_partition_hw(src_global, dst_local, cu_seqlens_global_dev, num_seqs, frames, H, W, split, rank,
                         stream=None):
     st = _lib.cpattn_partition_hw(ctypes.byref(_tensor(src_global)), ctypes.byref(_tensor(dst_local)),
-                                  _ptr(cu_seqlens_global_dev), num_seqs, frames, H, W, split[0], split[1], rank,
+                                  _cu(cu_seqlens_global_dev, "cu_seqlens_global", num_seqs), num_seqs, frames, H, W, split[0], split[1], rank,
                                   _stream(stream))
     _check(st, "cpattn_partition_hw")
 
@@ -266,7 +305,7 @@ def cpattn_partition_hw(src_global, dst_local, cu_seqlens_global_dev, num_seqs, 
 def cpattn_unpartition_hw(src_local, dst_global, cu_seqlens_global_dev, num_seqs, frames, H, W, split, rank,
                           stream=None):
     st = _lib.cpattn_unpartition_hw(ctypes.byref(_tensor(src_local)), ctypes.byref(_tensor(dst_global)),
-                                    _ptr(cu_seqlens_global_dev), num_seqs, frames, H, W, split[0], split[1], rank,
+                                    _cu(cu_seqlens_global_dev, "cu_seqlens_global", num_seqs), num_seqs, frames, H, W, split[0], split[1], rank,
                                     _stream(stream))
     _check(st, "cpattn_unpartition_hw")
 
@@ -294,6 +333,14 @@ def cpattn_count_pairs(cu_seqlens_global, mask_mode, step: Step) -> int:
     return int(n)
 
 
+def cpattn_step_source(step: Step) -> int:
+    """Rank whose K/V share the step uses: (rank - step) mod cp."""
+    j = _lib.cpattn_step_source(ctypes.byref(step))
+    if j < 0:
+        raise CpattnError(ERR_INVALID_ARG, "cpattn_step_source")
+    return int(j)
+
+
 def cpattn_workspace_size(tokens_q, tokens_k, num_seqs) -> int:
     return int(_lib.cpattn_workspace_size(tokens_q, tokens_k, num_seqs))
 
@@ -307,16 +354,20 @@ def cpattn_workspace_status(workspace, stream=None) -> int:
 
 def cpattn_fwd_step(q, k, v, cu_seqlens_q_dev, cu_seqlens_k_dev, num_seqs, mask_mode, step: Step,
                     softmax_scale, out_partial, lse_partial, workspace, stream=None):
+    ws, ws_bytes = _workspace(workspace)
     st = _lib.cpattn_fwd_step(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)), ctypes.byref(_tensor(v)),
-                              _ptr(cu_seqlens_q_dev), _ptr(cu_seqlens_k_dev), num_seqs, mask_mode,
+                              _cu(cu_seqlens_q_dev, "cu_seqlens_q", num_seqs),
+                              _cu(cu_seqlens_k_dev, "cu_seqlens_k", num_seqs), num_seqs, mask_mode,
                               ctypes.byref(step), float(softmax_scale), ctypes.byref(_tensor(out_partial)),
-                              _ptr(lse_partial), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), _stream(stream))
+                              _f32(lse_partial, "lse_partial", (q.shape[1], q.shape[0])), ws, ws_bytes,
+                              _stream(stream))
     _check(st, "cpattn_fwd_step")
 
 
 def cpattn_merge(out, lse, out_partial, lse_partial, stream=None):
-    st = _lib.cpattn_merge(_ptr(out), _ptr(lse), ctypes.byref(_tensor(out_partial)), _ptr(lse_partial),
+    t, h, d = out_partial.shape
+    st = _lib.cpattn_merge(_f32(out, "out", (t, h, d)), _f32(lse, "lse", (h, t)),
+                           ctypes.byref(_tensor(out_partial)), _f32(lse_partial, "lse_partial", (h, t)),
                            _stream(stream))
     _check(st, "cpattn_merge")
 
@@ -330,17 +381,24 @@ def cpattn_fill_f32(t, value: float, stream=None):
 
 
 def cpattn_bwd_preprocess(out, dout, delta, stream=None):
-    st = _lib.cpattn_bwd_preprocess(_ptr(out), ctypes.byref(_tensor(dout)), _ptr(delta), _stream(stream))
+    t, h, d = dout.shape
+    st = _lib.cpattn_bwd_preprocess(_f32(out, "out", (t, h, d)), ctypes.byref(_tensor(dout)),
+                                    _f32(delta, "delta", (h, t)), _stream(stream))
     _check(st, "cpattn_bwd_preprocess")
 
 
 def cpattn_bwd_step(q, k, v, dout, lse, delta, cu_seqlens_q_dev, cu_seqlens_k_dev, num_seqs, mask_mode,
                     step: Step, softmax_scale, dq_accum, dk_accum, dv_accum, workspace, stream=None):
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    ws, ws_bytes = _workspace(workspace)
     st = _lib.cpattn_bwd_step(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)), ctypes.byref(_tensor(v)),
-                              ctypes.byref(_tensor(dout)), _ptr(lse), _ptr(delta), _ptr(cu_seqlens_q_dev),
-                              _ptr(cu_seqlens_k_dev), num_seqs, mask_mode, ctypes.byref(step),
-                              float(softmax_scale), _ptr(dq_accum), _ptr(dk_accum), _ptr(dv_accum),
-                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+                              ctypes.byref(_tensor(dout)), _f32(lse, "lse", (hq, tq)), _f32(delta, "delta", (hq, tq)),
+                              _cu(cu_seqlens_q_dev, "cu_seqlens_q", num_seqs),
+                              _cu(cu_seqlens_k_dev, "cu_seqlens_k", num_seqs), num_seqs, mask_mode,
+                              ctypes.byref(step), float(softmax_scale), _f32(dq_accum, "dq", (tq, hq, d)),
+                              _f32(dk_accum, "dk", (tk, hkv, d)), _f32(dv_accum, "dv", (tk, hkv, d)),
+                              ws, ws_bytes, _stream(stream))
     _check(st, "cpattn_bwd_step")
 
 

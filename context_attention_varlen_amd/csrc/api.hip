@@ -114,6 +114,7 @@ SchedArgs sched_args(void* ws, const int32_t* cu_p, const int32_t* cu_s, int nse
   a.tile_p = tile_p;
   a.tile_s = tile_s;
   a.cost_mult = cost_mult;
+  a.tail_items = 0;
   a.max_items = (int32_t)max_items;
   char* base = (char*)ws;
   a.hdr = (WsHeader*)(base + R.hdr);
@@ -149,6 +150,7 @@ CPATTN_API const char* cpattn_status_string(cpattn_status s) {
     case CPATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case CPATTN_ERR_HIP: return "HIP runtime error";
     case CPATTN_ERR_INFEASIBLE: return "no feasible plan";
+    case CPATTN_ERR_NOMEM: return "out of host memory";
   }
   return "unknown status";
 }
@@ -439,6 +441,11 @@ CPATTN_API int64_t cpattn_count_pairs(const int32_t* cu_g, int32_t nseq, cpattn_
   return total;
 }
 
+CPATTN_API int32_t cpattn_step_source(const cpattn_step* st) {
+  if (!st || st->cp < 1 || st->rank < 0 || st->rank >= st->cp || st->step < 0 || st->step >= st->cp) return -1;
+  return src_rank(st);
+}
+
 CPATTN_API size_t cpattn_workspace_size(int64_t tokens_q, int64_t tokens_k, int32_t nseq) {
   if (tokens_q < 0 || tokens_k < 0 || nseq < 0) return 0;
   return ws_layout(tokens_q, tokens_k, nseq).total;
@@ -476,14 +483,19 @@ CPATTN_API cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_te
   const bool bf16 = q->dtype == CPATTN_BF16;
   const int d = q->head_dim;
   const int tile_p = fwd_tile_rows(bf16);
-  const int64_t max_items = sched_items(mode, step, q->tokens, nseq, tile_p);
+  // rows past cu_seqlens_q[nseq] (a padded buffer) get items with no keys,
+  // so every row of out_partial / lse_partial is written; the zigzag bound
+  // already counts them, the teacher-forcing one does not
+  const int64_t max_items = sched_items(mode, step, q->tokens, nseq, tile_p) +
+                            (tf_split(mode, step) ? (q->tokens + tile_p - 1) / tile_p : 0);
   if (max_items > ws_item_capacity(q->tokens, nseq)) return CPATTN_ERR_INVALID_ARG;
-  const SchedArgs sa = sched_args(ws, cu_q, cu_k, nseq, q->tokens, k->tokens, step, step->rank, src_rank(step),
-                                  true, mode, tile_p, 64, 1, max_items, L.a);
+  SchedArgs sa = sched_args(ws, cu_q, cu_k, nseq, q->tokens, k->tokens, step, step->rank, src_rank(step),
+                            true, mode, tile_p, 64, 1, max_items, L.a);
+  sa.tail_items = 1;
   hipStream_t s = (hipStream_t)stream;
   clear_stale_error();
   if ((st = hip_status(launch_sched(sa, s))) != CPATTN_OK) return st;
-  if (nseq == 0 || q->tokens == 0) return CPATTN_OK;
+  if (q->tokens == 0) return CPATTN_OK;
 
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)d);
   FwdArgs a;

@@ -60,6 +60,7 @@ struct SchedArgs {
   int32_t tile_p;        // primary tile rows
   int32_t tile_s;        // secondary tile rows (cost unit)
   int32_t cost_mult;     // cost multiplier (GQA group size for the dK/dV pass)
+  int32_t tail_items;    // 1: rows [cu_p[nseq], tokens_p) get items with no segments
   int32_t max_items;
   WsHeader* hdr;
   WorkItem* items;

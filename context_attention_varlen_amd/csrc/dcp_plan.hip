@@ -309,6 +309,9 @@ CPATTN_API cpattn_status cpattn_dcp_quotas(const int32_t* m, int32_t n, int32_t 
   return CPATTN_OK;
 }
 
+static cpattn_status plan_batch(const int32_t* lengths, int32_t n, const cpattn_dcp_config& c, int32_t nm,
+                                cpattn_dcp_plan* out);
+
 CPATTN_API cpattn_status cpattn_dcp_plan_batch(const int32_t* lengths, int32_t n, const cpattn_dcp_config* cfg,
                                                cpattn_dcp_plan* out) {
   if (!lengths || !cfg || !out || n < 1 || n > (1 << 24)) return CPATTN_ERR_INVALID_ARG;
@@ -327,6 +330,17 @@ CPATTN_API cpattn_status cpattn_dcp_plan_batch(const int32_t* lengths, int32_t n
       (int64_t)out->bucket_capacity < (int64_t)c.gpus * c.m_max)
     return CPATTN_ERR_INVALID_ARG;
 
+  // std::vector growth inside the planner can throw std::bad_alloc; no
+  // exception may cross the C boundary
+  try {
+    return plan_batch(lengths, n, c, nm, out);
+  } catch (...) {
+    return CPATTN_ERR_NOMEM;
+  }
+}
+
+static cpattn_status plan_batch(const int32_t* lengths, int32_t n, const cpattn_dcp_config& c, int32_t nm,
+                                cpattn_dcp_plan* out) {
   Planner pl(lengths, n, c);
   // Fig. 7 budget curve and its knee (IEEE double, order as written)
   const double floor_ = (double)pl.wmax() / (double)c.max_cp;

@@ -257,10 +257,16 @@ __device__ __forceinline__ void sched_body(const SchedArgs& a) {
     }
     carry += tot;
   }
+  // rows past the last sequence (a padded buffer): items without segments,
+  // so the forward still writes every row (0 and lse = -inf)
+  __shared__ int s_tail;
   if (tid == 0) {
     a.seq_base[a.nseq] = carry;
     if (a.nseq <= kLdsSeqs) s_seq_base[a.nseq] = carry;
-    if (carry > a.max_items) s_err = 1;
+    const int64_t end = a.nseq > 0 ? (int64_t)a.cu_p[a.nseq] : 0;
+    const int64_t rest = a.tail_items && end < a.tokens_p ? a.tokens_p - end : 0;
+    s_tail = (int)((rest + a.tile_p - 1) / a.tile_p);
+    if ((int64_t)carry + s_tail > a.max_items) s_err = 1;
   }
   __syncthreads();
   if (s_err) {
@@ -270,10 +276,27 @@ __device__ __forceinline__ void sched_body(const SchedArgs& a) {
     }
     return;
   }
-  const int n_items = carry;
+  const int n_seq_items = carry;
+  const int n_items = carry + s_tail;
 
   // ---- pass 2: build items -------------------------------------------------
   for (int idx = tid; idx < n_items; idx += kThreads) {
+    if (idx >= n_seq_items) {
+      const int end = a.nseq > 0 ? a.cu_p[a.nseq] : 0;
+      WorkItem it;
+      it.seq = a.nseq;
+      it.row0 = end + (idx - n_seq_items) * a.tile_p;
+      it.nrows = (int)min((int64_t)a.tile_p, a.tokens_p - it.row0);
+      it.pos0 = 0;
+      it.cost = 0;
+      it.nseg = 0;
+      it.seg[0] = Segment{0, 0, 0, 0, 0};
+      it.seg[1] = Segment{0, 0, 0, 0, 0};
+      a.items[idx] = it;
+      atomicAdd(&s_bins[0], 1);
+      if (idx < kLdsItems) s_bin_of[idx] = 0;
+      continue;
+    }
     // sequence: last b with seq_base[b] <= idx
     const int* sb = a.nseq <= kLdsSeqs ? s_seq_base : a.seq_base;
     int lo = 0, hi = a.nseq - 1;

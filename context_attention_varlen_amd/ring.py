@@ -18,7 +18,7 @@ import torch
 
 from . import (cpattn_bwd_preprocess, cpattn_bwd_step, cpattn_fill_f32, cpattn_fwd_step, cpattn_merge,
                cpattn_partition, cpattn_partition_index, cpattn_partition_index_tf, cpattn_partition_tf,
-               cpattn_workspace_size, make_step)
+               cpattn_step_source, cpattn_workspace_size, make_step)
 
 
 @dataclasses.dataclass
@@ -96,8 +96,8 @@ def ring_forward(q_local: torch.Tensor, k_shares: List[torch.Tensor], v_shares: 
         bufs.reset()
     partials = []
     for s in range(plan.cp):
-        j = (plan.rank - s) % plan.cp
         st = make_step(plan.cp, plan.rank, s, tf[0], tf[1])
+        j = cpattn_step_source(st)
         cpattn_fwd_step(q_local, k_shares[j], v_shares[j], plan.cu_local_dev, plan.cu_local_dev,
                         plan.num_seqs, mask_mode, st, scale, bufs.out_partial, bufs.lse_partial,
                         bufs.workspace)
@@ -125,8 +125,8 @@ def ring_backward(q_local, k_shares, v_shares, dout_local, bufs: ForwardBuffers,
             cpattn_fill_f32(x, 0.0)
     cpattn_bwd_preprocess(bufs.out, dout_local, delta)
     for s in range(plan.cp):
-        j = (plan.rank - s) % plan.cp
         st = make_step(plan.cp, plan.rank, s, tf[0], tf[1])
+        j = cpattn_step_source(st)
         cpattn_bwd_step(q_local, k_shares[j], v_shares[j], dout_local, bufs.lse, delta, plan.cu_local_dev,
                         plan.cu_local_dev, plan.num_seqs, mask_mode, st, scale, dq, dk[j], dv[j],
                         bufs.workspace)

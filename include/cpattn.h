@@ -74,7 +74,8 @@ typedef enum {
     CPATTN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (dtype, head_dim) */
     CPATTN_ERR_WORKSPACE = 3,     /* workspace missing or too small */
     CPATTN_ERR_HIP = 4,           /* a HIP runtime call or launch failed */
-    CPATTN_ERR_INFEASIBLE = 5     /* planner: no plan fits the memory cap */
+    CPATTN_ERR_INFEASIBLE = 5,    /* planner: no plan fits the memory cap */
+    CPATTN_ERR_NOMEM = 6          /* host memory for a planner call ran out */
 } cpattn_status;
 
 typedef enum { CPATTN_F32 = 0, CPATTN_BF16 = 1 } cpattn_dtype;
@@ -245,6 +246,14 @@ cpattn_status cpattn_head_to_seq(const cpattn_tensor* gathered, int32_t n_shards
 int64_t cpattn_count_pairs(const int32_t* cu_seqlens_global_host, int32_t num_seqs,
                            cpattn_mask_mode mask_mode, const cpattn_step* step);
 
+/* Source rank of a ring step: the rank whose K/V share rank step->rank holds
+ * at step step->step, (rank - step) mod cp ("Scaling Video Training with
+ * Parallelism", section 2, Ring Attention paragraph: the K/V blocks move one
+ * rank along the ring per step, so step 0 is the rank's own share).  The
+ * dK/dV accumulators cpattn_bwd_step adds into belong to this rank.  Host
+ * only; returns -1 for a NULL step or cp < 1 or rank/step outside [0, cp). */
+int32_t cpattn_step_source(const cpattn_step* step);
+
 /* ---- workspace -------------------------------------------------------------
  * Bytes of device workspace any call below needs for a rank with tokens_q
  * local query rows, tokens_k local key rows and num_seqs sequences. */
@@ -268,8 +277,10 @@ cpattn_status cpattn_workspace_status(const void* workspace, void* stream, cpatt
  *                and for CAUSAL / TF_BLOCK the per-sequence lengths of q and k
  *                must match (every rank's share has the same lengths); for
  *                CAUSAL at cp > 1 they are even (two zigzag chunks).
- *   out_partial  [Tq, Hq, d]      same dtype as q; every row of every sequence
- *                                 is overwritten (0 for rows with no key)
+ *   out_partial  [Tq, Hq, d]      same dtype as q; every row is overwritten
+ *                                 (0 for rows with no key, including rows
+ *                                 past cu_seqlens_q[num_seqs] in a padded
+ *                                 buffer)
  *   lse_partial_dev  fp32 [Hq][Tq]  (-inf for rows with no key)
  * Fully masked tiles are skipped by a device-side tile scheduler. */
 cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
@@ -279,6 +290,10 @@ cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_tensor* k, co
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- LSE merge -------------------------------------------------------------
+ * "Scaling Video Training with Parallelism", section 2, Ring Attention
+ * paragraph: each ring step yields attention over one K/V block, and the
+ * blocks' results are combined into attention over all keys (the page does
+ * not print the combination; this is the log-sum-exp union it implies).
  * Folds one step's partial result into the running result, in place, as the
  * softmax over the union of two disjoint key sets:
  *     lse' = log(exp(lse) + exp(lse_p))
@@ -301,12 +316,22 @@ cpattn_status cpattn_merge(float* out_dev, float* lse_dev, const cpattn_tensor* 
 cpattn_status cpattn_fill_f32(float* dst_dev, int64_t count, float value, void* stream);
 
 /* ---- backward --------------------------------------------------------------
- * delta_dev[h][t] = <dout[t,h,:], out[t,h,:]> with out the final merged fp32
- * output (dense [T][H][d]).  dout: [T, H, d] bf16 or fp32 view. */
+ * "Scaling Video Training with Parallelism", section 1: splitting a sample
+ * over ranks must leave the loss (and so its gradients) unchanged; the
+ * backward of the ring therefore differentiates attention over the whole
+ * sequence, one K/V share at a time, from the final merged O and LSE.
+ *
+ * Backward preprocess: delta_dev[h][t] = <dout[t,h,:], out[t,h,:]>, with out
+ * the final merged fp32 output (dense [T][H][d], all T*H rows read).
+ *   dout      [T, H, d] bf16 or fp32 view (T = dout->tokens)
+ *   delta_dev fp32 [H][T], written for every row
+ * INVALID_ARG for NULL or misaligned out/delta when T > 0. */
 cpattn_status cpattn_bwd_preprocess(const float* out_dev, const cpattn_tensor* dout,
                                     float* delta_dev, void* stream);
 
-/* One ring step of the backward, recomputing P from the saved final LSE:
+/* One ring step of the backward ("Scaling Video Training with Parallelism",
+ * section 1: the gradient of the unsplit loss; section 2: the same blockwise
+ * ring, one K/V share per step), recomputing P from the saved final LSE:
  *     P_ij = exp(scale <q_i,k_j> - lse_i),  dS_ij = P_ij (<dO_i,v_j> - delta_i)
  *     dq_accum[i]  += scale * sum_j dS_ij k_j
  *     dk_accum[j]  += scale * sum_i dS_ij q_i     (summed over a GQA group)

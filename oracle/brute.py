@@ -1,7 +1,7 @@
 """Pure-Python brute force for tiny inputs (oracle; test infrastructure only).
 
 Triple loops with math.fsum, written straight from the attention definition
-(see attention.py), used to pin the NumPy oracle on tiny shapes.  Masks are
+(softmax_attention.py), used to pin the NumPy oracle on tiny shapes.  Masks are
 passed in as a Python predicate so this file shares no mask code either.
 """
 import math

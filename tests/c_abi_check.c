@@ -40,6 +40,18 @@ int main(void) {
       st.tf_num_chunks = 0;
       CHECK(cpattn_count_pairs(cu, 1, CPATTN_MASK_CAUSAL, &st) == (s == 0 ? 2 * 32 * 32 + 32 : 2 * 32 * 32));
     }
+  /* ring source rule: (rank - step) mod cp, -1 for an invalid step */
+  for (r = 0; r < 4; ++r)
+    for (s = 0; s < 4; ++s) {
+      cpattn_step st;
+      st.cp = 4;
+      st.rank = r;
+      st.step = s;
+      st.tf_chunk_tokens = 0;
+      st.tf_num_chunks = 0;
+      CHECK(cpattn_step_source(&st) == (r - s + 4) % 4);
+    }
+  CHECK(cpattn_step_source(NULL) == -1);
   {
     int32_t sh = 0, sw = 0;
     CHECK(cpattn_split_hw(30, 52, 8, &sh, &sw) == CPATTN_OK);

@@ -106,6 +106,8 @@ def test_count_pairs_configs():
 class _FakeTensor:
     """Host-side stand-in with a data_ptr; the calls below fail validation
     before any device access."""
+    is_cuda = True
+
     def __init__(self, shape, dtype, ptr=0x1000, strides=None):
         import torch
         self.shape = shape
@@ -256,3 +258,38 @@ def test_count_pairs_bidir_any_split():
     cu = np.array([0, L], np.int32)
     for s in range(8):
         assert c.cpattn_count_pairs(cu, oracle.BIDIR, c.make_step(8, 3, s)) == (L // 8) ** 2
+
+
+def test_step_source_is_the_ring_rule():
+    """(rank - step) mod cp for every rank and step; -1 for invalid steps."""
+    for cp in (1, 2, 3, 4, 8):
+        for r in range(cp):
+            for s in range(cp):
+                assert c.cpattn_step_source(c.make_step(cp, r, s)) == oracle.step_source(cp, r, s)
+    for bad in (c.make_step(0, 0, 0), c.make_step(4, 4, 0), c.make_step(4, 0, 4), c.make_step(4, -1, 0)):
+        with pytest.raises(c.CpattnError):
+            c.cpattn_step_source(bad)
+
+
+def test_binding_rejects_host_arrays_and_wrong_dtypes():
+    """The binding checks what the raw-pointer arguments must be (device
+    memory, int32 cu_seqlens of num_seqs + 1 entries, fp32 [H, T] LSE) before
+    the C call; these raise without touching a GPU."""
+    import torch
+    with pytest.raises(ValueError):
+        c._tensor(torch.zeros((4, 2, 64), dtype=torch.bfloat16))          # host memory
+    cu64 = _FakeTensor((1, 1, 1), torch.int64)
+    cu64.shape = (3,)
+    with pytest.raises(ValueError):
+        c._cu(cu64, "cu", 2)                                              # int64 cu_seqlens
+    cu32 = _FakeTensor((1, 1, 1), torch.int32)
+    cu32.shape = (4,)
+    cu32.is_contiguous = lambda: True
+    with pytest.raises(ValueError):
+        c._cu(cu32, "cu", 2)                                              # num_seqs + 1 entries
+    lse = _FakeTensor((1, 1, 1), torch.float32)
+    lse.shape = (64, 4)
+    lse.is_contiguous = lambda: True
+    with pytest.raises(ValueError):
+        c._f32(lse, "lse", (4, 64))                                       # [T, H] instead of [H, T]
+    assert c._f32(lse, "lse", (64, 4)).value == lse.data_ptr()

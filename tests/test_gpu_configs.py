@@ -10,7 +10,8 @@ pytestmark = pytest.mark.gpu
 
 import oracle  # noqa: E402
 import workloads  # noqa: E402
-from tests._gpu import TOL_GRAD_RELRMS, check_lse, check_out, rel_rms, tdtype  # noqa: E402
+from tests._gpu import (TOL_GRAD_RELRMS, check_lse, check_out, oracle_by_head, rel_rms,  # noqa: E402
+                        stratified_offsets, tdtype)
 
 
 @pytest.fixture(scope="module")
@@ -49,9 +50,28 @@ def _sample_local_rows(w, r, count, seed):
     return np.unique(np.concatenate([base, np.asarray(extra, dtype=np.int64)]))
 
 
+def _stratified_local_rows(w, r, per_chunk, seed):
+    """At least `per_chunk` rows of every local chunk of rank r (each zigzag
+    half of each sequence): its first two and last two rows, rows next to
+    64- and 128-row tile edges (+-1), and uniform rows, seeded."""
+    cu_l, _, _, _ = oracle.local_rows(w.cu_seqlens, w.cp, r)
+    rng = np.random.default_rng(2000 + 10 * r + seed)
+    out = []
+    for b in range(len(cu_l) - 1):
+        n = int(cu_l[b + 1] - cu_l[b])
+        halves = [(int(cu_l[b]), n)] if w.cp == 1 else [(int(cu_l[b]), n // 2), (int(cu_l[b]) + n // 2, n // 2)]
+        for s0, m in halves:
+            if m:
+                out.append(s0 + stratified_offsets(m, per_chunk, rng))
+    return np.unique(np.concatenate(out))
+
+
 def _oracle_rows(w, x, r, rows, step=None):
     """Oracle output/LSE of a rank's sampled local rows: against every key of
-    their sequence (merged result) or only the keys of one ring step."""
+    their sequence (merged result) or only the keys of one ring step.  Under
+    the causal mask only keys up to the last sampled position can be allowed,
+    so the others are left out of the call (the result is the same).  Heads
+    run in parallel threads."""
     _, l2g, qpos, qseq = oracle.local_rows(w.cu_seqlens, w.cp, r)
     if step is None:
         seq, pos = _seq_pos(w.cu_seqlens)
@@ -59,8 +79,11 @@ def _oracle_rows(w, x, r, rows, step=None):
         kseq, kpos = seq[kidx], pos[kidx]
     else:
         _, kidx, kpos, kseq = oracle.local_rows(w.cu_seqlens, w.cp, oracle.step_source(w.cp, r, step))
-    return oracle.attention(x["q"][l2g[rows]], x["k"][kidx], x["v"][kidx], qseq[rows], qpos[rows], kseq, kpos,
-                            w.mask, tf_chunk=w.tf_chunk, tf_num=w.tf_num)
+    if w.mask == oracle.CAUSAL:
+        keep = kpos <= qpos[rows].max()
+        kidx, kpos, kseq = kidx[keep], kpos[keep], kseq[keep]
+    return oracle_by_head(oracle.attention, x["q"][l2g[rows]], x["k"][kidx], x["v"][kidx], qseq[rows], qpos[rows],
+                          kseq, kpos, w.mask, tf_chunk=w.tf_chunk, tf_num=w.tf_num)
 
 
 def _gpu_ring(w, x, r, keep=False, backward=False):
@@ -92,11 +115,14 @@ def long_video_inputs():
 @pytest.mark.parametrize("rank", [0, 7])
 def test_long_video_rank(cpa, long_video_inputs, rank):
     """262144 tokens, cp=8 zigzag, 28/4 heads: all 8 forward steps and merges
-    of one rank; sampled rows of the merged result and of two step partials."""
+    of one rank; at least 256 stratified rows of each of its two local chunks
+    (chunk edges, tile edges +-1, uniform) of the merged result and of three
+    step partials."""
     w = workloads.WORKLOADS["long_video"]
     x = long_video_inputs
     plan, bufs, parts, _ = _gpu_ring(w, x, rank, keep=True)
-    rows = _sample_local_rows(w, rank, 48, 0)
+    rows = _stratified_local_rows(w, rank, 256, 0)
+    assert len(rows) >= 512
     o_ref, l_ref = _oracle_rows(w, x, rank, rows)
     t = torch.from_numpy(rows).cuda()
     check_out(bufs.out[t].cpu().numpy(), o_ref, "bf16")
@@ -160,11 +186,39 @@ def test_tf_dit_sampled(cpa):
     check_lse(bufs.lse[:, t].cpu().numpy(), l_ref)
 
 
+def _oracle_rank_forward(w, x, r):
+    """fp64 O and LSE of every local row of rank r against every key of its
+    sequence, one local chunk at a time (under the causal mask a chunk's rows
+    can only see keys up to its last position, so later keys are left out of
+    the call); heads in parallel threads."""
+    cu = w.cu_seqlens
+    cu_l, l2g, qpos, qseq = oracle.local_rows(cu, w.cp, r)
+    seq, pos = _seq_pos(cu)
+    n = len(l2g)
+    o = np.zeros((n, w.heads_q, w.head_dim))
+    lse = np.full((w.heads_q, n), -np.inf)
+    for b in range(len(cu_l) - 1):
+        L = int(cu_l[b + 1] - cu_l[b])
+        for c0, m in ((int(cu_l[b]), L // 2), (int(cu_l[b]) + L // 2, L // 2)):
+            if m == 0:
+                continue
+            rows = np.arange(c0, c0 + m)
+            keys = np.nonzero((seq == b) & (pos <= qpos[rows].max()))[0]
+            o[rows], lse[:, rows] = oracle_by_head(oracle.attention, x["q"][l2g[rows]], x["k"][keys], x["v"][keys],
+                                                   qseq[rows], qpos[rows], seq[keys], pos[keys], w.mask)
+    return o, lse
+
+
 def test_long_tail_forward_backward(cpa):
-    """65536 tokens (49152 + 15 short), cp=4 zigzag, 32/8 heads, rank 0:
-    sampled forward rows; dQ on sampled query rows; dK/dV on sampled key rows
-    whose attending queries the oracle can enumerate (every short-sequence key
-    and the last keys of the long sequence); sum invariants over all keys."""
+    """65536 tokens (49152 + 15 short), cp=4 zigzag, 32/8 heads, rank 0, in
+    the launch configuration bench.py times.  The oracle computes the merged
+    forward of all 16384 local rows (so every row's output and LSE is
+    compared, and the exact LSE and delta feed the gradient checks); dQ on
+    512 stratified rows against every key; dK/dV of every source rank on at
+    least 256 stratified key rows of the 49152-token sequence (both chunk
+    halves, chunk and tile edges +-1, keys near the causal diagonal) and on
+    stratified keys of every short sequence, each summed over all of rank
+    0's queries; the gradient sums over all keys as an extra check."""
     w = workloads.WORKLOADS["long_tail"]
     x = workloads.draw(w)
     r = 0
@@ -174,43 +228,57 @@ def test_long_tail_forward_backward(cpa):
     cu_l, l2g, qpos, qseq = oracle.local_rows(cu, w.cp, r)
     seq, pos = _seq_pos(cu)
 
-    # forward and dQ on sampled rows
-    rows = _sample_local_rows(w, r, 40, 0)
-    o_ref, l_ref = _oracle_rows(w, x, r, rows)
-    t = torch.from_numpy(rows).cuda()
-    check_out(bufs.out[t].cpu().numpy(), o_ref, "bf16")
-    check_lse(bufs.lse[:, t].cpu().numpy(), l_ref)
+    # merged forward, every local row
+    o_ref, l_ref = _oracle_rank_forward(w, x, r)
+    check_out(bufs.out.cpu().numpy(), o_ref, "bf16")
+    check_lse(bufs.lse.cpu().numpy(), l_ref)
+    dout_l = x["dout"][l2g]
+    delta_ref = oracle.bwd_delta(o_ref, dout_l)
+
+    # dQ (summed over the 4 ring steps = every key) on stratified rows
+    rng = np.random.default_rng(3005)
+    rows = np.unique(np.concatenate([stratified_offsets(len(l2g), 384, rng),
+                                     _stratified_local_rows(w, r, 4, 1)]))
     kidx = np.nonzero(np.isin(seq, np.unique(qseq[rows])))[0]
-    delta = oracle.bwd_delta(o_ref, x["dout"][l2g[rows]])
-    dq_ref, _, _ = oracle.attention_backward(x["q"][l2g[rows]], x["k"][kidx], x["v"][kidx], x["dout"][l2g[rows]],
-                                             l_ref, delta, qseq[rows], qpos[rows], seq[kidx], pos[kidx], w.mask)
+    dq_ref, _, _ = oracle_by_head(oracle.attention_backward, x["q"][l2g[rows]], x["k"][kidx], x["v"][kidx],
+                                  dout_l[rows], l_ref[:, rows], delta_ref[:, rows], qseq[rows], qpos[rows],
+                                  seq[kidx], pos[kidx], w.mask)
+    t = torch.from_numpy(rows).cuda()
     assert rel_rms(dq[t].cpu().numpy(), dq_ref) <= TOL_GRAD_RELRMS
 
-    # dK/dV on keys of three short sequences (all of their rank-0 queries)
-    # and on the last 128 keys of the long sequence (its queries at the end)
-    for b, key_filter in ((1, None), (7, None), (15, None), (0, lambda p: p >= 49152 - 128)):
-        qrows = np.nonzero(qseq == b)[0]
-        if key_filter is not None:
-            qrows = qrows[qpos[qrows] >= 49152 - 128]
-        o_b, l_b = _oracle_rows(w, x, r, qrows)
-        d_b = oracle.bwd_delta(o_b, x["dout"][l2g[qrows]])
-        for s in range(w.cp):
-            j = oracle.step_source(w.cp, r, s)
-            _, k2g, kpos, kseq = oracle.local_rows(cu, w.cp, j)
-            ksel = np.nonzero(kseq == b)[0]
-            if key_filter is not None:
-                ksel = ksel[key_filter(kpos[ksel])]
-            if len(ksel) == 0:
-                continue
-            _, dk_ref, dv_ref = oracle.attention_backward(
-                x["q"][l2g[qrows]], x["k"][k2g[ksel]], x["v"][k2g[ksel]], x["dout"][l2g[qrows]], l_b, d_b,
-                qseq[qrows], qpos[qrows], kseq[ksel], kpos[ksel], w.mask)
+    # dK/dV per source rank, each sampled key summed over all rank-0 queries
+    # of its sequence
+    long_len = int(w.seqlens[0])
+    C = long_len // (2 * w.cp)
+    for j in range(w.cp):
+        _, k2g, kpos, kseq = oracle.local_rows(cu, w.cp, j)
+        krng = np.random.default_rng(4000 + j)
+        for b in range(len(w.seqlens)):
+            kb = np.nonzero(kseq == b)[0]
+            if b == 0:
+                half = len(kb) // 2
+                # both chunk halves: chunk / tile edges +-1 and uniform keys,
+                # plus keys next to rank 0's query-chunk boundaries (the
+                # causal diagonal of its chunks 0 and 2cp-1)
+                sel = [kb[:half][stratified_offsets(half, 160, krng)],
+                       kb[half:][stratified_offsets(half, 160, krng)]]
+                diag = np.nonzero(np.isin(kpos[kb], [C - 2, C - 1, C, (2 * w.cp - 1) * C - 1,
+                                                     (2 * w.cp - 1) * C, (2 * w.cp - 1) * C + 1,
+                                                     long_len - 2, long_len - 1]))[0]
+                ksel = np.unique(np.concatenate(sel + [kb[diag]]))
+                assert len(ksel) >= 256
+            else:
+                ksel = kb[stratified_offsets(len(kb), 24, krng)]
+            qrows = np.nonzero(qseq == b)[0]
+            _, dk_ref, dv_ref = oracle_by_head(
+                oracle.attention_backward, x["q"][l2g[qrows]], x["k"][k2g[ksel]], x["v"][k2g[ksel]], dout_l[qrows],
+                l_ref[:, qrows], delta_ref[:, qrows], qseq[qrows], qpos[qrows], kseq[ksel], kpos[ksel], w.mask)
             kt = torch.from_numpy(ksel).cuda()
-            assert rel_rms(dk[j][kt].cpu().numpy(), dk_ref) <= TOL_GRAD_RELRMS, (b, j)
-            assert rel_rms(dv[j][kt].cpu().numpy(), dv_ref) <= TOL_GRAD_RELRMS, (b, j)
+            assert rel_rms(dk[j][kt].cpu().numpy(), dk_ref) <= TOL_GRAD_RELRMS, ("dk", b, j)
+            assert rel_rms(dv[j][kt].cpu().numpy(), dv_ref) <= TOL_GRAD_RELRMS, ("dv", b, j)
 
-    # invariants over every key: sum_j dV_j = sum_i dO_i, sum_j dK_j = 0
-    do_loc = torch.from_numpy(x["dout"][l2g]).cuda()
+    # extra: sum_j dV_j = sum_i dO_i and sum_j dK_j = 0 over every key
+    do_loc = torch.from_numpy(dout_l).cuda()
     grp = w.heads_q // w.heads_kv
     for b in range(len(w.seqlens)):
         rs = slice(int(cu_l[b]), int(cu_l[b + 1]))
