@@ -30,7 +30,7 @@ EXPORTS = (
     "cpattn_seq_to_head", "cpattn_head_to_seq", "cpattn_split_hw", "cpattn_partition_index_hw",
     "cpattn_partition_hw", "cpattn_unpartition_hw",
     "cpattn_count_pairs", "cpattn_step_source", "cpattn_workspace_size", "cpattn_workspace_status",
-    "cpattn_fwd_step", "cpattn_merge", "cpattn_fill_f32", "cpattn_bwd_preprocess", "cpattn_bwd_step",
+    "cpattn_fwd_step", "cpattn_fwd_step_noalloc", "cpattn_merge", "cpattn_fill_f32", "cpattn_bwd_preprocess", "cpattn_bwd_step",
     "cpattn_dcp_plan_batch", "cpattn_dcp_quotas",
 )
 
@@ -106,6 +106,7 @@ def _load():
         "cpattn_workspace_size": (S, [I64, I64, I32]),
         "cpattn_workspace_status": (ctypes.c_int, [P, P, ctypes.POINTER(ctypes.c_int)]),
         "cpattn_fwd_step": (ctypes.c_int, [TP, TP, TP, P, P, I32, ctypes.c_int, SP, F, TP, P, P, S, P]),
+        "cpattn_fwd_step_noalloc": (ctypes.c_int, [TP, TP, TP, P, P, I32, ctypes.c_int, SP, F, TP, P, P]),
         "cpattn_merge": (ctypes.c_int, [P, P, TP, P, P]),
         "cpattn_fill_f32": (ctypes.c_int, [P, I64, F, P]),
         "cpattn_bwd_preprocess": (ctypes.c_int, [P, TP, P, P]),
@@ -362,6 +363,18 @@ def cpattn_fwd_step(q, k, v, cu_seqlens_q_dev, cu_seqlens_k_dev, num_seqs, mask_
                               _f32(lse_partial, "lse_partial", (q.shape[1], q.shape[0])), ws, ws_bytes,
                               _stream(stream))
     _check(st, "cpattn_fwd_step")
+
+
+def cpattn_fwd_step_noalloc(q, k, v, cu_seqlens_q_dev, cu_seqlens_k_dev, num_seqs, mask_mode, step: Step,
+                            softmax_scale, out_partial, lse_partial, stream=None):
+    """cpattn_fwd_step with the schedule workspace inside the library (no
+    device allocation by the call; see cpattn.h)."""
+    st = _lib.cpattn_fwd_step_noalloc(ctypes.byref(_tensor(q)), ctypes.byref(_tensor(k)), ctypes.byref(_tensor(v)),
+                                      _cu(cu_seqlens_q_dev, "cu_seqlens_q", num_seqs),
+                                      _cu(cu_seqlens_k_dev, "cu_seqlens_k", num_seqs), num_seqs, mask_mode,
+                                      ctypes.byref(step), float(softmax_scale), ctypes.byref(_tensor(out_partial)),
+                                      _f32(lse_partial, "lse_partial", (q.shape[1], q.shape[0])), _stream(stream))
+    _check(st, "cpattn_fwd_step_noalloc")
 
 
 def cpattn_merge(out, lse, out_partial, lse_partial, stream=None):

@@ -1,9 +1,11 @@
 // libcpattn C ABI: argument validation and dispatch.  Every entry point
 // checks its arguments before anything is enqueued; no C++ exception leaves
 // this file.
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "common.h"
@@ -461,11 +463,10 @@ CPATTN_API cpattn_status cpattn_workspace_status(const void* ws, void* stream, c
   return CPATTN_OK;
 }
 
-CPATTN_API cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
-                                         const int32_t* cu_q, const int32_t* cu_k, int32_t nseq,
-                                         cpattn_mask_mode mode, const cpattn_step* step, float scale,
-                                         cpattn_tensor* out, float* lse, void* ws, size_t ws_bytes,
-                                         void* stream) {
+static cpattn_status fwd_step_impl(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                   const int32_t* cu_q, const int32_t* cu_k, int32_t nseq, cpattn_mask_mode mode,
+                                   const cpattn_step* step, float scale, cpattn_tensor* out, float* lse, void* ws,
+                                   size_t ws_bytes, void* stream) {
   cpattn_status st;
   if ((st = check_tensor(q)) || (st = check_tensor(k)) || (st = check_tensor(v)) || (st = check_tensor(out)))
     return st;
@@ -521,6 +522,63 @@ CPATTN_API cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_te
   a.items = sa.items;
   a.order = sa.order;
   return hip_status(launch_fwd(a, bf16, d, max_items, s));
+}
+
+CPATTN_API cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                         const int32_t* cu_q, const int32_t* cu_k, int32_t nseq,
+                                         cpattn_mask_mode mode, const cpattn_step* step, float scale,
+                                         cpattn_tensor* out, float* lse, void* ws, size_t ws_bytes,
+                                         void* stream) {
+  return fwd_step_impl(q, k, v, cu_q, cu_k, nseq, mode, step, scale, out, lse, ws, ws_bytes, stream);
+}
+
+// ---- allocation-free forward step ------------------------------------------
+// The schedule workspace of cpattn_fwd_step_noalloc lives in this file-scope
+// device array; every GPU the library runs on holds its own copy for the
+// life of the process.  In host code `scratch` only names the symbol: its
+// device address on the current GPU comes from hipGetSymbolAddress, resolved
+// once per device and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[CPATTN_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+cpattn_status scratch_ptr(void** out) {
+  int dev = -1;
+  cpattn_status st;
+  if ((st = hip_status(hipGetDevice(&dev))) != CPATTN_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return CPATTN_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      // the device that is current now is the one whose copy is resolved
+      if ((st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)))) != CPATTN_OK) return st;
+      if (!p) return CPATTN_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return CPATTN_OK;
+}
+
+}  // namespace
+
+CPATTN_API cpattn_status cpattn_fwd_step_noalloc(const cpattn_tensor* q, const cpattn_tensor* k,
+                                                 const cpattn_tensor* v, const int32_t* cu_q, const int32_t* cu_k,
+                                                 int32_t nseq, cpattn_mask_mode mode, const cpattn_step* step,
+                                                 float scale, cpattn_tensor* out, float* lse, void* stream) {
+  // size check first: a shape beyond the array is refused before any HIP call
+  if (!q || !k || q->tokens < 0 || k->tokens < 0 || nseq < 0) return CPATTN_ERR_INVALID_ARG;
+  if (ws_layout(q->tokens, k->tokens, nseq).total > (size_t)CPATTN_SCRATCH_BYTES) return CPATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  cpattn_status st;
+  if ((st = scratch_ptr(&ws)) != CPATTN_OK) return st;
+  return fwd_step_impl(q, k, v, cu_q, cu_k, nseq, mode, step, scale, out, lse, ws, CPATTN_SCRATCH_BYTES, stream);
 }
 
 CPATTN_API cpattn_status cpattn_merge(float* out, float* lse, const cpattn_tensor* op, const float* lsep,

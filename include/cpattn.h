@@ -289,6 +289,28 @@ cpattn_status cpattn_fwd_step(const cpattn_tensor* q, const cpattn_tensor* k, co
                               float softmax_scale, cpattn_tensor* out_partial, float* lse_partial_dev,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- allocation-free forward step -------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation as cpattn_fwd_step, with the schedule workspace taken from a
+ * device array inside the library instead of a caller buffer.  The array is
+ * CPATTN_SCRATCH_BYTES per GPU, held from the library's first call on that
+ * GPU until the process ends; a shape whose cpattn_workspace_size(Tq, Tk,
+ * num_seqs) exceeds it returns CPATTN_ERR_WORKSPACE before anything is
+ * enqueued (16 MiB covers about 1.9M local query rows with as many key rows).
+ * The call allocates nothing.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (two streams, two threads) race and must be
+ * ordered by the caller.  Nothing in the array needs clearing between calls.
+ * A bad device cu_seqlens array leaves out_partial / lse_partial untouched,
+ * as for cpattn_fwd_step; its status stays in the array, unreported.
+ * Arguments and outputs otherwise as cpattn_fwd_step. */
+#define CPATTN_SCRATCH_BYTES (16 * 1024 * 1024)
+cpattn_status cpattn_fwd_step_noalloc(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                                      const int32_t* cu_seqlens_q_dev, const int32_t* cu_seqlens_k_dev,
+                                      int32_t num_seqs, cpattn_mask_mode mask_mode, const cpattn_step* step,
+                                      float softmax_scale, cpattn_tensor* out_partial, float* lse_partial_dev,
+                                      void* stream);
+
 /* ---- LSE merge -------------------------------------------------------------
  * "Scaling Video Training with Parallelism", section 2, Ring Attention
  * paragraph: each ring step yields attention over one K/V block, and the

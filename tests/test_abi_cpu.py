@@ -293,3 +293,19 @@ def test_binding_rejects_host_arrays_and_wrong_dtypes():
     with pytest.raises(ValueError):
         c._f32(lse, "lse", (4, 64))                                       # [T, H] instead of [H, T]
     assert c._f32(lse, "lse", (64, 4)).value == lse.data_ptr()
+
+
+def test_noalloc_forward_rejects_oversized_shapes():
+    """The allocation-free forward refuses a shape whose schedule workspace
+    exceeds the library's array before any HIP call (so this runs on CPU)."""
+    import torch
+    import context_attention_varlen_amd as m
+    big = 4_000_000
+    assert c.cpattn_workspace_size(big, big, 1) > (16 << 20)
+    q = _FakeTensor((big, 1, 128), torch.bfloat16)
+    st = c.make_step(1, 0, 0)
+    rc = m._lib.cpattn_fwd_step_noalloc(ctypes.byref(m._tensor(q)), ctypes.byref(m._tensor(q)),
+                                        ctypes.byref(m._tensor(q)), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x2000),
+                                        1, 0, ctypes.byref(st), 0.0, ctypes.byref(m._tensor(q)),
+                                        ctypes.c_void_p(0x3000), None)
+    assert rc == c.ERR_WORKSPACE
