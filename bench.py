@@ -329,7 +329,9 @@ def _time_rank_share(c, torch, pool, lens, cp, reps=2):
     T = sum(loc)
     cu = torch.tensor(np.concatenate([[0], np.cumsum(loc)]).astype(np.int32), device="cuda")
     q, k, v, do = (pool[n][:T] for n in ("q", "k", "v", "do"))
-    dq, dk, dv, delta = pool["dq"][:T], pool["dk"][:T], pool["dv"][:T], pool["delta"][:, :T]
+    # delta is [Hq, T] contiguous: a view of the front of a flat buffer
+    dq, dk, dv = pool["dq"][:T], pool["dk"][:T], pool["dv"][:T]
+    delta = pool["delta"][:pool["q"].shape[1] * T].view(pool["q"].shape[1], T)
     bufs = ForwardBuffers.make(q, T, len(lens))
     steps = [c.make_step(cp, 0, s) for s in range(cp)]
 
@@ -377,7 +379,7 @@ def dynamic_cp_extra(c, torch, gen):
     pool = {n: torch.randn((MEM, Hq if n in ("q", "do") else Hkv, d), device="cuda", generator=gen).bfloat16()
             for n in ("q", "k", "v", "do")}
     pool.update({"dq": torch.zeros((MEM, Hq, d), device="cuda"), "dk": torch.zeros((MEM, Hkv, d), device="cuda"),
-                 "dv": torch.zeros((MEM, Hkv, d), device="cuda"), "delta": torch.zeros((Hq, MEM), device="cuda")})
+                 "dv": torch.zeros((MEM, Hkv, d), device="cuda"), "delta": torch.zeros(Hq * MEM, device="cuda")})
 
     samples = []     # (sum S^2 / cp, sum S / cp, ms) per timed microbatch share
 

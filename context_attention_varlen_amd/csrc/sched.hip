@@ -128,20 +128,27 @@ __device__ int build_segments(const SchedArgs& a, int p0, int p1, const int* cb,
     return ns;
   }
   // primary = keys [p0, p1)
-  if (has_clean) {
-    const int ck_lo = p0 / B, ck_hi = (min(p1, span) - 1) / B;
-    // clean queries of chunks >= ck_lo
-    set_seg(seg[ns++], base, 0, ck_lo * B, span, has_noisy ? 0 : ck_hi * B, has_noisy ? 0 : span);
-    // noisy queries of chunks > ck (clean keys) ...
-    int lo = span + (ck_lo + 1) * B, hi = L;
-    int flo = has_noisy ? 0 : span + (ck_hi + 1) * B, fhi = has_noisy ? 0 : L;
-    if (has_noisy) {
-      // ... together with noisy queries of the noisy keys' own chunks
-      const int nk_lo = (max(p0, span) - span) / B, nk_hi = (p1 - 1 - span) / B;
-      lo = min(lo, span + nk_lo * B);
-      hi = max(min(hi, L), span + (nk_hi + 1) * B);
+  if (has_clean && has_noisy) {
+    // the tile straddles the stream boundary: its noisy keys are chunks
+    // 0..nk_hi.  Clean queries of chunks >= ck_lo and noisy queries of
+    // chunks <= nk_hi form one run [ck_lo*B, span + (nk_hi+1)*B); noisy
+    // queries of chunks > ck_lo (which see the clean keys) add the suffix
+    // past it.  Every row of both runs attends some key of the tile.
+    const int ck_lo = p0 / B, nk_hi = (p1 - 1 - span) / B;
+    const int run_hi = span + (nk_hi + 1) * B, suf_lo = span + (ck_lo + 1) * B;
+    if (suf_lo <= run_hi) {
+      set_seg(seg[ns++], base, 0, ck_lo * B, max(run_hi, suf_lo < L ? L : run_hi), 0, 0);
+    } else {
+      set_seg(seg[ns++], base, 0, ck_lo * B, run_hi, 0, 0);
+      if (suf_lo < L) set_seg(seg[ns++], base, 0, suf_lo, L, 0, 0);
     }
-    if (lo < hi) set_seg(seg[ns++], base, 0, lo, hi, flo, fhi);
+  } else if (has_clean) {
+    const int ck_lo = p0 / B, ck_hi = (p1 - 1) / B;
+    // clean queries of chunks >= ck_lo (all keys for chunks >= ck_hi)
+    set_seg(seg[ns++], base, 0, ck_lo * B, span, ck_hi * B, span);
+    // noisy queries of chunks > ck_lo (all keys for chunks > ck_hi)
+    const int lo = span + (ck_lo + 1) * B;
+    if (lo < L) set_seg(seg[ns++], base, 0, lo, L, span + (ck_hi + 1) * B, L);
   } else {
     const int nk_lo = (p0 - span) / B, nk_hi = (p1 - 1 - span) / B;
     const int lo = span + nk_lo * B, hi = span + (nk_hi + 1) * B;
