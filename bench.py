@@ -424,6 +424,93 @@ def dynamic_cp_extra(c, torch, gen):
             "calibrated_ns_per_S2": round(float(coef[0]) * 1e6, 6), "calibrated_ns_per_token": round(float(coef[1]) * 1e6, 3)}
 
 
+def long_video_step(c, torch, steps=5, warmup=1):
+    """The long-video rank's whole step as its own measurement: zigzag
+    partition of Q (rank 0) and of K/V for all 8 source ranks, then 8 x
+    (tile scheduler + forward step + LSE merge), 262144 tokens at cp = 8,
+    28/4 heads, d = 128, bf16.  Inputs are device-random (only time counts;
+    the parity tests check this shape against the oracle).  Per-call times
+    are HIP events on the launch stream; the forward kernel and the merge
+    get their roofline objects (merge: algorithmic bytes of the rows that are
+    live in each step)."""
+    import workloads
+    from context_attention_varlen_amd.ring import ForwardBuffers, RankPlan
+    w = workloads.WORKLOADS["long_video"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    plan = RankPlan.make(w.cu_seqlens, w.cp, w.rank)
+    mk = lambda h: (torch.randn((w.tokens, h, w.head_dim), device="cuda", generator=gen)  # noqa: E731
+                    * w.value_scale).bfloat16()
+    qg, kg, vg = mk(w.heads_q), mk(w.heads_kv), mk(w.heads_kv)
+    tl = plan.tokens_local
+    q = torch.empty((tl, w.heads_q, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    ks = [torch.empty((tl, w.heads_kv, w.head_dim), dtype=torch.bfloat16, device="cuda") for _ in range(w.cp)]
+    vs = [torch.empty_like(ks[0]) for _ in range(w.cp)]
+    bufs = ForwardBuffers.make(q, tl, plan.num_seqs)
+    sts = [c.make_step(w.cp, w.rank, s) for s in range(w.cp)]
+    cu_g, cu_l, nseq = plan.cu_global_dev, plan.cu_local_dev, plan.num_seqs
+
+    def step(tm):
+        tm("partition", lambda: c.cpattn_partition(qg, q, cu_g, nseq, w.cp, w.rank))
+        for j in range(w.cp):
+            tm("partition", lambda j=j: c.cpattn_partition(kg, ks[j], cu_g, nseq, w.cp, j))
+            tm("partition", lambda j=j: c.cpattn_partition(vg, vs[j], cu_g, nseq, w.cp, j))
+        bufs.reset()
+        for s in range(w.cp):
+            j = c.cpattn_step_source(sts[s])
+            tm("fwd_step", lambda s=s, j=j: c.cpattn_fwd_step(q, ks[j], vs[j], cu_l, cu_l, nseq, w.mask, sts[s], 0.0,
+                                                             bufs.out_partial, bufs.lse_partial, bufs.workspace))
+            tm("merge", lambda: c.cpattn_merge(bufs.out, bufs.lse, bufs.out_partial, bufs.lse_partial))
+
+    null = lambda name, fn: fn()  # noqa: E731
+    for _ in range(warmup):
+        step(null)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step(tm)
+    b.record()
+    torch.cuda.synchronize()
+    ws_status = c.cpattn_workspace_status(bufs.workspace)
+    if ws_status != c.OK:
+        raise SystemExit(f"bench: the tile scheduler rejected the long-video batch: {c.status_string(ws_status)}")
+    ms = a.elapsed_time(b) / steps
+    st = tm.stats()
+    pairs = [c.cpattn_count_pairs(w.cu_seqlens, w.mask, x) for x in sts]
+    flops = 4 * w.head_dim * w.heads_q * sum(pairs)
+    fwd = st["fwd_step"]
+    f_avg = fwd["avg_ms"]
+    f_ach = flops / w.cp / (f_avg * 1e-3) / 1e12
+    # merge bytes: 8d + 2d + 12 per live (token, head) row, 4 per skipped row;
+    # on rank 0 every row is live at step 0 and only the second chunk after
+    live0 = tl * w.heads_q
+    live_s = (tl // 2) * w.heads_q
+    m_bytes = [live0 * (10 * w.head_dim + 12)] + [live_s * (10 * w.head_dim + 12) + (tl * w.heads_q - live_s) * 4
+                                                   for _ in range(w.cp - 1)]
+    mg = st["merge"]
+    m_ach = sum(m_bytes) / (mg["total_ms"] / steps * 1e-3) / 1e9
+    del qg, kg, vg, q, ks, vs, bufs
+    torch.cuda.empty_cache()
+    return {
+        "workload": "long_video: 262144 tokens, causal zigzag cp=8 rank 0, Hq=28/Hkv=4, d=128, bf16; "
+                    "partition + 8 x (scheduler + forward step + merge)",
+        "steps": steps, "ms_per_step": round(ms, 4), "pairs_per_head": sum(pairs), "flops_per_step": flops,
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+        "pct_of_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "per_call_ms_per_step": {k: round(v["total_ms"] / steps, 4) for k, v in st.items()},
+        "roofline": {"bound": "mfma", "kernel": "cpattn::fwd_bf16_kernel<128, 4>", "achieved": round(f_ach, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(f_ach / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(f_avg, 4),
+                     "algorithmic_flops_per_launch": int(flops / w.cp)},
+        "merge_roofline": {"bound": "hbm", "kernel": "cpattn::merge_kernel<128, true>", "achieved": round(m_ach, 1),
+                           "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(m_ach / PEAK_HBM_GBPS, 4),
+                           "traffic": None, "avg_launch_ms": round(mg["avg_ms"], 4),
+                           "algorithmic_bytes_per_step": int(sum(m_bytes))},
+    }
+
+
 def extras(c, torch):
     """Forward and merge figures of the other workloads (not part of `value`)."""
     import workloads
@@ -651,6 +738,8 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(w, x)
         note("cpu baseline done")
     if not args.no_extras:
+        rec["long_video_step"] = long_video_step(c, torch)
+        note("long-video step done")
         rec["extras"] = extras(c, torch)
     print(json.dumps(rec), flush=True)
 
