@@ -237,7 +237,7 @@ def run_hot_path(c, torch, w, steps, warmup, graph=True):
 
 def graph_step_ms(torch, step, null, steps):
     """After the timed region: the same step captured once as a HIP graph and
-    replayed `steps` times (every call only enqueues kernels, so it captures
+    replayed max(steps, 100) times (every call only enqueues kernels, so it captures
     as is).  None if this torch build cannot capture."""
     try:
         side = torch.cuda.Stream()
@@ -253,13 +253,16 @@ def graph_step_ms(torch, step, null, steps):
         print(f"graph capture unavailable: {e}", file=sys.stderr, flush=True)
         return None
     graph.replay()
+    # at least 100 replays (about 2 s of the long-tail step), so that a
+    # sampler of GPU activity sees the step running, not only host work
+    reps = max(steps, 100)
     ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ea.record()
-    for _ in range(steps):
+    for _ in range(reps):
         graph.replay()
     eb.record()
     torch.cuda.synchronize()
-    return ea.elapsed_time(eb) / steps
+    return ea.elapsed_time(eb) / reps
 
 
 def cpu_baseline(w, x, rows=512):
@@ -723,7 +726,7 @@ def main():
         "pairs_per_head": P, "flops_per_step": fwd_flops + bwd_flops, "outputs_finite": finite,
         "per_call": per_call, "roofline": roofline, "roofline_other_attention_kernel": roofline_other,
         # not `value`: the same step captured once as a HIP graph and replayed
-        # `steps` times after the timed region (no per-call launch gaps)
+        # max(steps, 100) times after the timed region (no per-call launch gaps)
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": round(graph_ms, 4), "tflops": round((fwd_flops + bwd_flops) / (graph_ms * 1e-3) / 1e12, 2)},
     }
@@ -734,13 +737,14 @@ def main():
                      "arch": torch.cuda.get_device_properties(0).gcnArchName, "cus": cus,
                      "peak_clock_mhz": khz / 1000,
                      "bf16_peak_at_peak_clock_tflops": round(cus * 4096 * khz * 1e3 / 1e12, 1)}
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, x)
-        note("cpu baseline done")
+    # GPU phases first, the host-only oracle baseline last
     if not args.no_extras:
         rec["long_video_step"] = long_video_step(c, torch)
         note("long-video step done")
         rec["extras"] = extras(c, torch)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, x)
+        note("cpu baseline done")
     print(json.dumps(rec), flush=True)
 
 
