@@ -49,6 +49,8 @@ def parse():
                    help="skip the graph-replay figure (counter runs: only the timed steps dispatch)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a device copy of a known size (reference for HBM byte counters)")
+    p.add_argument("--gemm-ceiling", action="store_true",
+                   help="run only the library bf16 GEMM ceiling (torch.matmul) and print it")
     p.add_argument("--write-traffic", nargs=4, metavar=("CAL_FETCH", "CAL_WRITE", "RUN_FETCH", "RUN_WRITE"),
                    help="CPU only: turn four rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE of "
                         "--copy-calibration, then of a --steps 2 --warmup 0 --no-extras run) into "
@@ -637,6 +639,33 @@ def extras(c, torch):
     return out
 
 
+def gemm_ceiling(torch):
+    """The vendor library's dense bf16 GEMM rate on this GPU (torch.matmul,
+    which dispatches to hipBLASLt), timed with events: the practical ceiling
+    a matrix-core kernel meets under the chip's power limit, beside the
+    nominal 2.5 PFLOP/s."""
+    out = {"kernel": "torch.matmul bf16 (hipBLASLt)"}
+    for n, reps in ((8192, 20), (16384, 6)):
+        a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+        b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            a @ b
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"gemm_{n}_cubed"] = {"ms": round(ms, 4), "tflops": round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
+        del a, b
+    torch.cuda.empty_cache()
+    out["tflops"] = max(v["tflops"] for k, v in out.items() if k.startswith("gemm_"))
+    out["pct_of_bf16_peak"] = round(100 * out["tflops"] / PEAK_BF16_TFLOPS, 1)
+    return out
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -661,6 +690,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 4 * n, "bytes_written_per_copy": 4 * n,
                                                "copies": 4}}), flush=True)
+        return
+    if args.gemm_ceiling:
+        print(json.dumps({"gemm_ceiling": gemm_ceiling(torch)}), flush=True)
         return
     import context_attention_varlen_amd as c
     import workloads
@@ -742,6 +774,14 @@ def main():
         rec["long_video_step"] = long_video_step(c, torch)
         note("long-video step done")
         rec["extras"] = extras(c, torch)
+        # the library GEMM on the same box, and the attention kernels' matrix
+        # work against it (the backward executes 7 products per pair, 5 credited)
+        ceil = gemm_ceiling(torch)
+        ceil["fwd_over_gemm"] = round(per_call["fwd_step"]["tflops"] / ceil["tflops"], 3)
+        if "bwd_step" in st:
+            ceil["bwd_executed_over_gemm"] = round(per_call["bwd_step"]["tflops"] * 7 / 5 / ceil["tflops"], 3)
+        rec["practical_ceiling"] = ceil
+        note("gemm ceiling done")
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x)
         note("cpu baseline done")

@@ -2,6 +2,9 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
 #include <stdint.h>
 
 #include "cpattn.h"
@@ -327,6 +330,55 @@ __device__ __forceinline__ KeyRanges query_ranges(int mode, int32_t pk, int32_t 
 
 __device__ __forceinline__ bool in_ranges(const KeyRanges& r, int32_t pk) {
   return ((unsigned)pk - r.lo1 < r.len1) | ((unsigned)pk - r.lo2 < r.len2);
+}
+
+// A KeyRanges as two position windows [lo, end) with end saturated to
+// INT_MAX.  For the intervals key_ranges and query_ranges produce (lo below
+// 2^31, and lo = 0 whenever len exceeds 2^31) a position p >= 0 is allowed
+// iff it lies in one of the windows: the same predicate as in_ranges.
+struct KeyWindows {
+  int lo1, end1, lo2, end2;
+};
+
+__device__ __forceinline__ KeyWindows key_windows(const KeyRanges& r) {
+  auto end = [](unsigned lo, unsigned len) {
+    const unsigned long long e = (unsigned long long)lo + len;
+    return e > 0x7fffffffull ? 0x7fffffff : (int)e;
+  };
+  return KeyWindows{(int)r.lo1, end(r.lo1, r.len1), (int)r.lo2, end(r.lo2, r.len2)};
+}
+
+// The predicate for the positions pbase + k, k < 28 (the offsets a lane's
+// accumulator block holds), as a bit set: bit k is set iff k < rem and
+// pbase + k lies in a window.  Each window becomes the offset range
+// [lo - pbase, end - pbase) clipped to [0, min(rem, 28)), so a masked block
+// costs one bit test per element instead of the range tests.
+__device__ __forceinline__ unsigned allowed_bits(const KeyWindows& w, int32_t pbase, int32_t rem) {
+  const int lim = min(max(rem, 0), 28);
+  auto window = [&](int lo, int end) {
+    const int a = min(max(lo - pbase, 0), lim);
+    const int b = min(max(end - pbase, a), lim);
+    return ((1u << (b - a)) - 1u) << a;
+  };
+  return window(w.lo1, w.end1) | window(w.lo2, w.end2);
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, each index a constant
+template <class F, int... I>
+__device__ __forceinline__ void for_each_index_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void for_each_index(F&& f) {
+  for_each_index_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// v where bit K of `bits` is set, else the bit pattern `off`: a
+// sign-extended one-bit field and a bit-field select.
+template <int K>
+__device__ __forceinline__ float select_bit(unsigned bits, float v, unsigned off) {
+  const unsigned m = (unsigned)__builtin_amdgcn_sbfe((int)bits, K, 1);
+  return __uint_as_float((__float_as_uint(v) & m) | (off & ~m));
 }
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -67,8 +67,12 @@ void fwd_bf16_kernel(FwdArgs a) {
   constexpr int NS = 2 * NK;       // S^T products per tile (two key blocks)
   constexpr int NP = 4 * (D / 32); // PV products per tile
   constexpr int PF = kFwdPF;
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][BN * D];
+  // Four separate arrays (not one [2][..] array per operand): every buffer
+  // index below is a compile-time constant, so the compiler can tell a read
+  // of one buffer from the direct loads still filling the other and does
+  // not wait for those loads before the read.
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[BN * D], s_k1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v0[BN * D], s_v1[BN * D];
 
   int item_rank, h, g;
   map_block(blockIdx.x, a.grp, a.hkv, item_rank, h, g, items_per_unit(a.grp));
@@ -77,6 +81,10 @@ void fwd_bf16_kernel(FwdArgs a) {
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int col = lane & 31, hh = lane >> 5;
+  // lane parts of the K row reads (k-step parity 0, 1) and the V^T reads
+  const int lko[2] = {opaque_lane(tile_off_lane<D>(col, hh)), opaque_lane(tile_off_lane<D>(col, 2 ^ hh))};
+  int lvo[2];
+  tr_lane_offsets<D>(lane, lvo);
   const int64_t kst = a.k_st * 2, vst = a.v_st * 2;
   const char* kbase = (const char*)a.k + (int64_t)g * a.k_sh * 2;
   const char* vbase = (const char*)a.v + (int64_t)g * a.v_sh * 2;
@@ -92,27 +100,22 @@ void fwd_bf16_kernel(FwdArgs a) {
     t0 = (j - (s ? nt0 : 0)) * BN;
     sg = it.seg[s];
   };
-  auto issue_k = [&](int j) {
+  // tile j goes to buffer j & 1; `buf` is that buffer (a constant at each call)
+  auto issue_k = [&](int j, uint16_t* buf) {
     int t0;
     Segment sg;
     tile_at(j, t0, sg);
-    lk.issue(s_k[j & 1], kbase + (int64_t)(sg.row + t0) * kst, min(BN, sg.n - t0), kst);
+    lk.issue(buf, kbase + (int64_t)(sg.row + t0) * kst, min(BN, sg.n - t0), kst);
   };
-  auto issue_v = [&](int j) {
+  auto issue_v = [&](int j, uint16_t* buf) {
     int t0;
     Segment sg;
     tile_at(j, t0, sg);
-    lv.issue(s_v[j & 1], vbase + (int64_t)(sg.row + t0) * vst, min(BN, sg.n - t0), vst);
+    lv.issue(buf, vbase + (int64_t)(sg.row + t0) * vst, min(BN, sg.n - t0), vst);
   };
-  if (ntiles > 0) {
-    issue_k(0);
-    issue_v(0);
-    if (ntiles > 1) issue_k(1);
-  }
-
   const int r = wave * 32 + col;
   const bool row_ok = r < it.nrows;
-  const KeyRanges kr = key_ranges(a.mask, it.pos0 + r, a.tf_b, a.tf_n);
+  const KeyWindows kw = key_windows(key_ranges(a.mask, it.pos0 + r, a.tf_b, a.tf_n));
   bf16x8 qreg[NK];
   {
     const uint16_t* src = (const uint16_t*)a.q + (int64_t)(it.row0 + r) * a.q_st + (int64_t)h * a.q_sh + 8 * hh;
@@ -122,6 +125,15 @@ void fwd_bf16_kernel(FwdArgs a) {
       if (row_ok) raw = *(const u32x4*)(src + 16 * ks);
       qreg[ks] = __builtin_bit_cast(bf16x8, raw);
     }
+  }
+  // Q is loaded before the first K/V tiles, so the prologue's wait for
+  // K(0) (vmcnt counts in issue order) also covers Q and leaves V(0) and
+  // K(1) in flight; the fence keeps the compiler from sinking the Q loads.
+  asm volatile("" ::: "memory");
+  if (ntiles > 0) {
+    issue_k(0, s_k0);
+    issue_v(0, s_v0);
+    if (ntiles > 1) issue_k(1, s_k1);
   }
   f32x16 acc_o[D / 32];
 #pragma unroll
@@ -136,13 +148,11 @@ void fwd_bf16_kernel(FwdArgs a) {
   // mask of a partial tile, then its scaled row max
   auto mask_block = [&](f32x16 (&st)[2], int kb, int t0, const Segment& sg) {
     const int kbase0 = t0 + 32 * kb + 4 * hh;
-    const int rem = sg.n - kbase0;
-    const int pbase = sg.pos + kbase0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int off = 8 * (i >> 2) + (i & 3);
-      st[kb][i] = ((off < rem) & in_ranges(kr, pbase + off)) ? st[kb][i] : -INFINITY;
-    }
+    const unsigned bits = allowed_bits(kw, sg.pos + kbase0, sg.n - kbase0);
+    for_each_index<16>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      st[kb][i] = select_bit<8 * (i >> 2) + (i & 3)>(bits, st[kb][i], 0xff800000u);
+    });
   };
   auto rowmax_part = [&](const f32x16& v, float m) {
     m = max3f(m, v[0], v[1]);
@@ -154,14 +164,17 @@ void fwd_bf16_kernel(FwdArgs a) {
   // prologue: S^T of tile 0 with its mask and row max
   if (ntiles > 0) {
     wait_vmcnt_tiles<TileLoader<D, BN, NW>::PER>(ntiles > 1 ? 2 : 1);   // K(0) in; V(0), K(1) may load
-    __syncthreads();
+    // a bare barrier: __syncthreads() would also wait for V(0) and K(1)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[0][kb][i] = 0.f;
 #pragma unroll
     for (int u = 0; u < NS; ++u)
-      sacc[0][u / NK] = mfma32(read_row8<D>(s_k[0], 32 * (u / NK), col, u % NK, hh), qreg[u % NK], sacc[0][u / NK]);
+      sacc[0][u / NK] = mfma32(read_row8_at<D>(s_k0, lko[(u % NK) & 1], 32 * (u / NK), u % NK), qreg[u % NK], sacc[0][u / NK]);
     int t0;
     Segment sg;
     tile_at(0, t0, sg);
@@ -180,10 +193,10 @@ void fwd_bf16_kernel(FwdArgs a) {
     constexpr bool more = decltype(morec)::value;
     wait_loads();                                  // K(j+1), V(j) in (issued an iteration ago)
     __syncthreads();
-    if (j + 2 < ntiles) issue_k(j + 2);            // into K(j)'s buffer
-    if (more) issue_v(j + 1);                      // into V(j-1)'s buffer
-    const uint16_t* tk = s_k[Q];
-    const uint16_t* tv = s_v[P];
+    if (j + 2 < ntiles) issue_k(j + 2, P ? s_k1 : s_k0);   // into K(j)'s buffer
+    if (more) issue_v(j + 1, Q ? s_v1 : s_v0);             // into V(j-1)'s buffer
+    const uint16_t* tk = Q ? s_k1 : s_k0;
+    const uint16_t* tv = P ? s_v1 : s_v0;
     int t1 = 0;
     Segment sg1 = it.seg[0];
     if (more) tile_at(j + 1, t1, sg1);
@@ -242,9 +255,9 @@ void fwd_bf16_kernel(FwdArgs a) {
 
     // ---- products ----------------------------------------------------------
     bf16x8 kop[NS], vop[NP];
-    auto read_k = [&](int u) { kop[u] = read_row8<D>(tk, 32 * (u / NK), col, u % NK, hh); };
+    auto read_k = [&](int u) { kop[u] = read_row8_at<D>(tk, lko[(u % NK) & 1], 32 * (u / NK), u % NK); };
     auto read_v = [&](int m) {          // PV product m: k-step pair ps = m / (D/32), d-block m % (D/32)
-      vop[m] = read_tr<D>(tv, 16 * (m / (D / 32)), 32 * (m % (D / 32)), lane);
+      vop[m] = read_tr_at<D>(tv, lvo, 16 * (m / (D / 32)), 32 * (m % (D / 32)));
     };
     auto read_op = [&](int x) {         // operand x of the iteration's product sequence
       if (x < NS) { if (more) read_k(x); }

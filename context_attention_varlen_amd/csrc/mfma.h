@@ -151,6 +151,61 @@ __device__ __forceinline__ bf16x8 read_row8(const uint16_t* tile, int rc, int rl
   return __builtin_bit_cast(bf16x8, *(__attribute__((address_space(3))) const u32x4*)p);
 }
 
+// tile_off_split as a constant part plus a lane part:
+//   tile_off_split(rc, rl, cg, cl) == tile_off_const(rc, cg) + tile_off_lane(rl, cl ^ ((rc >> 2) & 3))
+template <int D>
+__device__ __forceinline__ int tile_off_const(int rc, int cg) {
+  constexpr int LRG = D == 128 ? 2 : 3;
+  return (int)((((unsigned)rc >> LRG) << 9) + (unsigned)cg * (32u << LRG));
+}
+template <int D>
+__device__ __forceinline__ int tile_off_lane(int rl, int cl) { return tile_off_split<D>(0, rl, 0, cl); }
+
+// A lane offset the optimizer cannot take apart.  Reads built as
+// tile + opaque lane offset + constant keep every constant in the
+// instruction's immediate offset and stay a short address chain from their
+// LDS variable, so the compiler can tell a read of one LDS variable from
+// direct loads still filling another and waits for the loads only where
+// the buffers are the same.
+__device__ __forceinline__ int opaque_lane(int x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
+// read_row8 of k-step ks at tile row rc + (the lane's row), with lane_off
+// = tile_off_lane(row, (2 * (ks & 1)) ^ hh) (rc a multiple of 16)
+template <int D>
+__device__ __forceinline__ bf16x8 read_row8_at(const uint16_t* tile, int lane_off, int rc, int ks) {
+  lds_u16* p = lds_ptr(tile) + lane_off + tile_off_const<D>(rc, ks >> 1);
+  return __builtin_bit_cast(bf16x8, *(__attribute__((address_space(3))) const u32x4*)p);
+}
+
+// read_tr with the lane parts precomputed: lane_off[t] =
+// tile_off_lane(4hh + j/4, (2mh + (j%4)/2) ^ 2t) + 4(j%2) (r0 a multiple of 16)
+template <int D>
+__device__ __forceinline__ bf16x8 read_tr_at(const uint16_t* tile, const int (&lane_off)[2], int r0, int c0) {
+  s16x4 v[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    v[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(lds_ptr(tile) + lane_off[t] + tile_off_const<D>(r0 + 8 * t, c0 >> 5)));
+  u32x4 r;
+  r[0] = __builtin_bit_cast(u32x2, v[0])[0];
+  r[1] = __builtin_bit_cast(u32x2, v[0])[1];
+  r[2] = __builtin_bit_cast(u32x2, v[1])[0];
+  r[3] = __builtin_bit_cast(u32x2, v[1])[1];
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// The two lane offsets read_tr_at needs for this lane
+template <int D>
+__device__ __forceinline__ void tr_lane_offsets(int lane, int (&lane_off)[2]) {
+  const int j = lane & 15, mh = (lane >> 4) & 1, hh = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    lane_off[t] = opaque_lane(tile_off_lane<D>(4 * hh + (j >> 2), (2 * mh + ((j & 3) >> 1)) ^ (2 * t)) + 4 * (j & 1));
+}
+
 // Transposed operand: the 32 x 16 operand whose MFMA row index runs along
 // tile columns [c0, c0 + 32) and whose k index runs along tile rows
 // [r0, r0 + 16).  With ds_read_b64_tr_b16, lane j of each 16-lane group
