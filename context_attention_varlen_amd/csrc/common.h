@@ -149,6 +149,7 @@ struct FwdArgs {
   const WsHeader* hdr;
   const WorkItem* items;
   const int32_t* order;
+  int order_cap;       // entries the order array holds (the scheduler's item bound)
 };
 
 struct BwdArgs {

@@ -76,8 +76,13 @@ void fwd_bf16_kernel(FwdArgs a) {
 
   int item_rank, h, g;
   map_block(blockIdx.x, a.grp, a.hkv, item_rank, h, g, items_per_unit(a.grp));
-  if (item_rank >= a.hdr->n_items) return;
-  const WorkItem it = a.items[a.order[item_rank]];
+  // the item count and the item's order entry load together (the entry is
+  // read in bounds, and dropped for a rank past the count)
+  const int n_items = a.hdr->n_items;
+  const int oi = a.order[min(item_rank, a.order_cap - 1)];
+  asm volatile("" ::"s"(oi), "s"(n_items));   // both loads issued before the test
+  if (item_rank >= n_items) return;
+  const WorkItem it = a.items[oi];
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int col = lane & 31, hh = lane >> 5;
@@ -311,19 +316,44 @@ void fwd_bf16_kernel(FwdArgs a) {
 
   const float l = sum_halves(l_run);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (!row_ok) return;
-  uint16_t* op = (uint16_t*)a.out + (int64_t)(it.row0 + r) * a.o_st + (int64_t)h * a.o_sh;
+  // O leaves through LDS so that every store writes whole rows: each wave
+  // puts its 32 rows into a block of its own, 16-byte chunks swizzled by row
+  // (conflict-free writes down a column), and reads them back row-major.
+  // The K buffers are free here: the last iteration reads only V, and all
+  // waves passed its barrier after their last K read.
+  // (The lane index is recomputed here rather than kept live through the
+  // tile loop, where the register file is full.)
+  const int ln = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int ecol = ln & 31, ehh = ln >> 5;
+  {
+    constexpr int CH = D / 8;                                // 16-byte chunks per row
+    constexpr int RPI = 64 / CH;                             // rows per read instruction
+    char* blk = (char*)((wave < 2 ? s_k0 : s_k1) + (wave & 1) * 32 * D);
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      bf16x4 w;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc_o[db][4 * i4 + e] * inv);
-      *(u32x2*)(op + db * 32 + 8 * i4 + 4 * hh) = __builtin_bit_cast(u32x2, w);
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc_o[db][4 * i4 + e] * inv);
+        const int chunk = db * 4 + i4;
+        *(u32x2*)(blk + ecol * (2 * D) + ((chunk ^ (ecol & (CH - 1))) << 4) + 8 * ehh) = __builtin_bit_cast(u32x2, w);
+      }
+    const int rl = ln / CH, ch = ln % CH;
+    u32x4 v[32 / RPI];
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+      const int rr = k * RPI + rl;                           // row within the wave's 32
+      v[k] = *(const u32x4*)(blk + rr * (2 * D) + ((ch ^ (rr & (CH - 1))) << 4));
     }
-  if (hh == 0)
-    a.lse[(int64_t)h * a.tq + it.row0 + r] = l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
+    uint16_t* orow = (uint16_t*)a.out + (int64_t)(it.row0 + wave * 32 + rl) * a.o_st + (int64_t)h * a.o_sh + 8 * ch;
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k)
+      if (wave * 32 + k * RPI + rl < it.nrows) *(u32x4*)(orow + (int64_t)(k * RPI) * a.o_st) = v[k];
+  }
+  if (ehh == 0 && wave * 32 + ecol < it.nrows)
+    a.lse[(int64_t)h * a.tq + it.row0 + wave * 32 + ecol] =
+        l > 0.f ? (m_run + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -380,7 +410,9 @@ constexpr int kFwdTile = 32 * kFwdWaves;   // query rows per workgroup
 
 int fwd_tile_rows(bool bf16) { return bf16 ? kFwdTile : 64; }
 
-hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, int64_t max_items, hipStream_t stream) {
+hipError_t launch_fwd(const FwdArgs& a0, bool bf16, int d, int64_t max_items, hipStream_t stream) {
+  FwdArgs a = a0;
+  a.order_cap = (int)max_items;
   const dim3 grid(unit_grid(max_items, a.hkv, a.grp, bf16 ? items_per_unit(a.grp) : 1));
   if (bf16) {
     if (d == 128) hipLaunchKernelGGL((fwd_bf16_kernel<128, kFwdWaves>), grid, dim3(64 * kFwdWaves), 0, stream, a);
