@@ -160,10 +160,9 @@ void fwd_bf16_kernel(FwdArgs a) {
     });
   };
   auto rowmax_part = [&](const f32x16& v, float m) {
-    m = max3f(m, v[0], v[1]);
 #pragma unroll
-    for (int i = 2; i + 1 < 16; i += 2) m = max3f(m, v[i], v[i + 1]);
-    return fmaxf(m, v[15]);
+    for (int i = 0; i < 16; i += 2) m = max3f(m, v[i], v[i + 1]);
+    return m;
   };
 
   // prologue: S^T of tile 0 with its mask and row max

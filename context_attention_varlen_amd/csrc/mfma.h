@@ -106,9 +106,13 @@ struct TileLoader {
 
 // Max of a value over the two 32-lane halves of the wave (the C-layout rows
 // of one accumulator column live in lanes l and l^32).
+// (v_max_f32 written out: fmaxf would first canonicalize both inputs, two
+// more instructions, since the compiler cannot tell they are not NaNs)
 __device__ __forceinline__ float max_halves(float x) {
   const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(__uint_as_float(pr[0])), "v"(__uint_as_float(pr[1])));
+  return r;
 }
 
 __device__ __forceinline__ float sum_halves(float x) {
