@@ -256,7 +256,7 @@ __device__ __forceinline__ int32_t zigzag_pos(int32_t off, int32_t len, int32_t 
 }
 
 // The mask predicate on in-sequence positions (query pq, key pk).
-__device__ __forceinline__ bool mask_allowed(int mode, int32_t pq, int32_t pk, int32_t tf_b, int32_t tf_n) {
+__host__ __device__ inline bool mask_allowed(int mode, int32_t pq, int32_t pk, int32_t tf_b, int32_t tf_n) {
   if (mode == CPATTN_MASK_CAUSAL) return pk <= pq;
   if (mode == CPATTN_MASK_BIDIR) return true;
   const int32_t span = tf_b * tf_n;
@@ -274,7 +274,7 @@ struct KeyRanges {
   unsigned lo1, len1, lo2, len2;
 };
 
-__device__ __forceinline__ KeyRanges key_ranges(int mode, int32_t pq, int32_t tf_b, int32_t tf_n) {
+__host__ __device__ inline KeyRanges key_ranges(int mode, int32_t pq, int32_t tf_b, int32_t tf_n) {
   KeyRanges r;
   r.lo2 = 0u;
   r.len2 = 0u;
@@ -302,7 +302,7 @@ __device__ __forceinline__ KeyRanges key_ranges(int mode, int32_t pq, int32_t tf
 
 // The queries that may attend a key at position pk (the transpose of
 // key_ranges), as at most two position intervals.
-__device__ __forceinline__ KeyRanges query_ranges(int mode, int32_t pk, int32_t tf_b, int32_t tf_n) {
+__host__ __device__ inline KeyRanges query_ranges(int mode, int32_t pk, int32_t tf_b, int32_t tf_n) {
   KeyRanges r;
   r.lo2 = 0u;
   r.len2 = 0u;
@@ -329,7 +329,7 @@ __device__ __forceinline__ KeyRanges query_ranges(int mode, int32_t pk, int32_t 
   return r;
 }
 
-__device__ __forceinline__ bool in_ranges(const KeyRanges& r, int32_t pk) {
+__host__ __device__ inline bool in_ranges(const KeyRanges& r, int32_t pk) {
   return ((unsigned)pk - r.lo1 < r.len1) | ((unsigned)pk - r.lo2 < r.len2);
 }
 
@@ -341,7 +341,7 @@ struct KeyWindows {
   int lo1, end1, lo2, end2;
 };
 
-__device__ __forceinline__ KeyWindows key_windows(const KeyRanges& r) {
+__host__ __device__ inline KeyWindows key_windows(const KeyRanges& r) {
   auto end = [](unsigned lo, unsigned len) {
     const unsigned long long e = (unsigned long long)lo + len;
     return e > 0x7fffffffull ? 0x7fffffff : (int)e;
@@ -354,7 +354,7 @@ __device__ __forceinline__ KeyWindows key_windows(const KeyRanges& r) {
 // pbase + k lies in a window.  Each window becomes the offset range
 // [lo - pbase, end - pbase) clipped to [0, min(rem, 28)), so a masked block
 // costs one bit test per element instead of the range tests.
-__device__ __forceinline__ unsigned allowed_bits(const KeyWindows& w, int32_t pbase, int32_t rem) {
+__host__ __device__ inline unsigned allowed_bits(const KeyWindows& w, int32_t pbase, int32_t rem) {
   const int lim = min(max(rem, 0), 28);
   auto window = [&](int lo, int end) {
     const int a = min(max(lo - pbase, 0), lim);
