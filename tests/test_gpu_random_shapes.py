@@ -27,18 +27,21 @@ def cpa():
     return c
 
 
-def _draw(seed):
-    rng = np.random.default_rng(20000 + seed)
+def _draw(seed, long=False):
+    """One case.  long: fewer, longer sequences (700-4000 tokens), so that
+    items run tens of key tiles and dK/dV workgroups sweep ~100 query tiles,
+    element by element against the oracle."""
+    rng = np.random.default_rng((60000 if long else 20000) + seed)
     hq, hkv = [(2, 1), (4, 2), (3, 3), (8, 2), (6, 3)][int(rng.integers(0, 5))]
     d = int(rng.choice([64, 128]))
     if rng.random() < 0.2:
         # teacher forcing at cp = 1 (cp > 1 has its own tests): 1-2 sequences
         # of [clean ; noisy] with random chunk size B and count N
-        B, N = int(rng.integers(1, 120)), int(rng.integers(1, 6))
+        B, N = int(rng.integers(1, 600 if long else 120)), int(rng.integers(1, 6))
         return [2 * B * N] * int(rng.integers(1, 3)), 1, 0, hq, hkv, d, oracle.TF_BLOCK, (B, N)
     cp = int(rng.choice([1, 2, 3, 4]))
     mode = oracle.CAUSAL if rng.random() < 0.7 else oracle.BIDIR
-    nseq = int(rng.integers(1, 7))
+    nseq = int(rng.integers(1, 4 if long else 7))
     quantum = 2 * cp
     lens = []
     for _ in range(nseq):
@@ -48,7 +51,7 @@ def _draw(seed):
         elif kind < 0.35:
             n = int(rng.integers(1, 40))
         else:
-            n = int(rng.integers(40, 700))
+            n = int(rng.integers(700, 4000)) if long else int(rng.integers(40, 700))
         lens.append(n - n % quantum if cp > 1 else n)
     if sum(lens) == 0:
         lens[0] = 8 * quantum
@@ -56,9 +59,7 @@ def _draw(seed):
     return lens, cp, rank, hq, hkv, d, mode, (0, 0)
 
 
-@pytest.mark.parametrize("seed", range(160))
-def test_random_shape(cpa, seed):
-    lens, cp, r, hq, hkv, d, mode, tf = _draw(seed)
+def _check_case(lens, cp, r, hq, hkv, d, mode, tf, seed):
     print(f"seed {seed}: lens {lens} cp {cp} rank {r} heads {hq}/{hkv} d {d} mode {mode} tf {tf}", flush=True)
     x, cu = _inputs(300 + seed, lens, hq, hkv, d, "bf16")
     dq, dk, dv, delta, bufs = run_gpu(x, cu, cp, r, mode, "bf16", tf)
@@ -75,6 +76,16 @@ def test_random_shape(cpa, seed):
     for j in range(cp):
         _check_grad(dk[j], dk_r[j], f"dk[{j}]")
         _check_grad(dv[j], dv_r[j], f"dv[{j}]")
+
+
+@pytest.mark.parametrize("seed", range(400))
+def test_random_shape(cpa, seed):
+    _check_case(*_draw(seed), seed)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shape_long(cpa, seed):
+    _check_case(*_draw(seed, long=True), 1000 + seed)
 
 
 @pytest.mark.parametrize("seed", range(16))
