@@ -131,3 +131,115 @@ def ring_backward(q_local, k_shares, v_shares, dout_local, bufs: ForwardBuffers,
                         plan.cu_local_dev, plan.num_seqs, mask_mode, st, scale, dq, dk[j], dv[j],
                         bufs.workspace)
     return dq, dk, dv, delta
+
+
+@dataclasses.dataclass
+class StepBuffers:
+    """Device buffers of one rank's whole step: the gathered shares, the
+    forward state (with a second partial pair, so a merge can overlap the
+    next forward step) and the fp32 gradients."""
+    q: torch.Tensor
+    dout: Optional[torch.Tensor]
+    ks: List[torch.Tensor]
+    vs: List[torch.Tensor]
+    fwd: ForwardBuffers
+    partial2: tuple
+    dq: Optional[torch.Tensor]
+    dk: Optional[List[torch.Tensor]]
+    dv: Optional[List[torch.Tensor]]
+    delta: Optional[torch.Tensor]
+
+    @staticmethod
+    def make(plan: RankPlan, heads_q: int, heads_kv: int, head_dim: int, dtype, backward: bool,
+             device="cuda") -> "StepBuffers":
+        tl = plan.tokens_local
+        q = torch.empty((tl, heads_q, head_dim), dtype=dtype, device=device)
+        ks = [torch.empty((tl, heads_kv, head_dim), dtype=dtype, device=device) for _ in range(plan.cp)]
+        vs = [torch.empty_like(ks[0]) for _ in range(plan.cp)]
+        fb = ForwardBuffers.make(q, tl, plan.num_seqs)
+        p2 = (torch.empty_like(fb.out_partial), torch.empty_like(fb.lse_partial))
+        if not backward:
+            return StepBuffers(q, None, ks, vs, fb, p2, None, None, None, None)
+        f32 = dict(dtype=torch.float32, device=device)
+        return StepBuffers(q, torch.empty_like(q), ks, vs, fb, p2, torch.empty(q.shape, **f32),
+                           [torch.empty(ks[0].shape, **f32) for _ in range(plan.cp)],
+                           [torch.empty(ks[0].shape, **f32) for _ in range(plan.cp)],
+                           torch.empty((heads_q, tl), **f32))
+
+
+def _gather(x_global: torch.Tensor, dst: torch.Tensor, plan: RankPlan, rank: int):
+    if plan.tf[0]:
+        cpattn_partition_tf(x_global, dst, plan.cu_global_dev, plan.num_seqs, plan.cp, rank, plan.tf[0], plan.tf[1])
+    else:
+        cpattn_partition(x_global, dst, plan.cu_global_dev, plan.num_seqs, plan.cp, rank)
+
+
+def rank_step(q_g: torch.Tensor, k_g: torch.Tensor, v_g: torch.Tensor, dout_g: Optional[torch.Tensor],
+              plan: RankPlan, mask_mode: int, b: StepBuffers, side: Optional[torch.cuda.Stream] = None,
+              scale: float = 0.0):
+    """One rank's whole step from the global THD tensors: gathers of Q (and
+    dO) and of every source rank's K/V share, cp forward steps with their LSE
+    merges, then (when dout_g is given) the backward preprocess and cp
+    backward steps into b.dq / b.dk / b.dv.
+
+    With `side` (a stream of default priority) the work that the ring would
+    overlap with compute runs there, ordered by events: the K/V gathers of
+    steps 1.. (the ring's transfers), the dO gather, the gradient zero fills
+    and the merges, which alternate between two partial buffers so that merge
+    s runs beside forward step s + 1.  Every buffer sees the same kernels in
+    the same order either way, so the results are bit-identical; the calling
+    stream is joined with `side` before the backward and at the end.  Only
+    enqueues work, so it can be captured as a graph."""
+    cp, r = plan.cp, plan.rank
+    tf = plan.tf
+    steps = [make_step(cp, r, s, tf[0], tf[1]) for s in range(cp)]
+    src = [cpattn_step_source(st) for st in steps]
+    main = torch.cuda.current_stream()
+    fb = b.fwd
+    parts = [(fb.out_partial, fb.lse_partial), b.partial2] if side is not None else [(fb.out_partial, fb.lse_partial)]
+    _gather(q_g, b.q, plan, r)
+    _gather(k_g, b.ks[src[0]], plan, src[0])
+    _gather(v_g, b.vs[src[0]], plan, src[0])
+    fb.reset()
+    ready = {}
+    if side is not None:
+        side.wait_stream(main)
+    with torch.cuda.stream(side if side is not None else main):
+        for s in range(1, cp):
+            _gather(k_g, b.ks[src[s]], plan, src[s])
+            _gather(v_g, b.vs[src[s]], plan, src[s])
+            if side is not None:
+                ready[s] = torch.cuda.Event()
+                ready[s].record(side)
+        if dout_g is not None:
+            _gather(dout_g, b.dout, plan, r)
+            for x in [b.dq] + b.dk + b.dv:
+                cpattn_fill_f32(x, 0.0)
+    merged = {}
+    for s in range(cp):
+        if s in ready:
+            main.wait_event(ready[s])
+        if s >= 2 and side is not None:
+            main.wait_event(merged[s - 2])    # partial buffer s % 2 is free again
+        op, lp = parts[s % len(parts)]
+        cpattn_fwd_step(b.q, b.ks[src[s]], b.vs[src[s]], plan.cu_local_dev, plan.cu_local_dev, plan.num_seqs,
+                        mask_mode, steps[s], scale, op, lp, fb.workspace)
+        if side is None:
+            cpattn_merge(fb.out, fb.lse, op, lp)
+            continue
+        done = torch.cuda.Event()
+        done.record(main)
+        with torch.cuda.stream(side):
+            side.wait_event(done)
+            cpattn_merge(fb.out, fb.lse, op, lp)
+            merged[s] = torch.cuda.Event()
+            merged[s].record(side)
+    if side is not None:
+        main.wait_stream(side)
+    if dout_g is None:
+        return
+    cpattn_bwd_preprocess(fb.out, b.dout, b.delta)
+    for s in range(cp):
+        cpattn_bwd_step(b.q, b.ks[src[s]], b.vs[src[s]], b.dout, fb.lse, b.delta, plan.cu_local_dev,
+                        plan.cu_local_dev, plan.num_seqs, mask_mode, steps[s], scale, b.dq, b.dk[src[s]],
+                        b.dv[src[s]], fb.workspace)
