@@ -24,7 +24,7 @@ same bit for bit.  The same calls issued eagerly on one stream, one host call
 per kernel with events around each call, give the per-kernel figures and are
 reported beside it.
 
-Prints one JSON line.  Only N=1 is measured: this build targets one GPU.
+Prints one JSON line.  Only N=1 is measured: the library runs one rank's share on one GPU.
 """
 import argparse
 import hashlib
@@ -722,7 +722,7 @@ def main():
         write_traffic(*args.write_traffic)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs one rank's share "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library runs one rank's share "
               "on one MI355X and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import torch
