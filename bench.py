@@ -824,7 +824,7 @@ def main():
             "replays": gr["extra_replays"], "ms_per_step": round(gr["extra_ms_per_step"], 4),
             "tflops": round((fwd_flops + bwd_flops) / (gr["extra_ms_per_step"] * 1e-3) / 1e12, 2)},
     }
-    # the box's own figures: CU count and peak shader clock, and the dense
+    # the device's own figures: CU count and peak shader clock, and the dense
     # bf16 matrix-core peak they give (4096 FLOP per clock per CU on gfx950)
     cus, khz = c.cpattn_device_info(torch.cuda.current_device())
     rec["device"] = {"name": torch.cuda.get_device_properties(0).name,
@@ -836,7 +836,7 @@ def main():
         rec["long_video_step"] = long_video_step(c, torch)
         note("long-video step done")
         rec["extras"] = extras(c, torch)
-        # the library GEMM on the same box, and the attention kernels' matrix
+        # the library GEMM on the same device, and the attention kernels' matrix
         # work against it (the backward executes 7 products per pair, 5 credited)
         ceil = gemm_ceiling(torch)
         ceil["fwd_over_gemm"] = round(per_call["fwd_step"]["tflops"] / ceil["tflops"], 3)
