@@ -176,7 +176,7 @@ def _gather(x_global: torch.Tensor, dst: torch.Tensor, plan: RankPlan, rank: int
 
 def rank_step(q_g: torch.Tensor, k_g: torch.Tensor, v_g: torch.Tensor, dout_g: Optional[torch.Tensor],
               plan: RankPlan, mask_mode: int, b: StepBuffers, side: Optional[torch.cuda.Stream] = None,
-              scale: float = 0.0):
+              scale: float = 0.0, tf=None):
     """One rank's whole step from the global THD tensors: gathers of Q (and
     dO) and of every source rank's K/V share, cp forward steps with their LSE
     merges, then (when dout_g is given) the backward preprocess and cp
@@ -189,9 +189,11 @@ def rank_step(q_g: torch.Tensor, k_g: torch.Tensor, v_g: torch.Tensor, dout_g: O
     s runs beside forward step s + 1.  Every buffer sees the same kernels in
     the same order either way, so the results are bit-identical; the calling
     stream is joined with `side` before the backward and at the end.  Only
-    enqueues work, so it can be captured as a graph."""
+    enqueues work, so it can be captured as a graph.  tf = (B, N) gives the
+    teacher-forcing mask's chunking (default: the plan's split; needed at
+    cp = 1, where the plan has no split)."""
     cp, r = plan.cp, plan.rank
-    tf = plan.tf
+    tf = plan.tf if tf is None else tf
     steps = [make_step(cp, r, s, tf[0], tf[1]) for s in range(cp)]
     src = [cpattn_step_source(st) for st in steps]
     main = torch.cuda.current_stream()

@@ -153,3 +153,24 @@ def test_random_balanced_tf_split(cpa, seed):
     for j in range(cp):
         assert rel_rms(dk[j].cpu().numpy(), dk_r[j]) <= TOL_GRAD_RELRMS, j
         assert rel_rms(dv[j].cpu().numpy(), dv_r[j]) <= TOL_GRAD_RELRMS, j
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shape_overlapped_step(cpa, seed):
+    """ring.rank_step with its second stream on the random draws gives bit
+    for bit what the one-stream ring calls give (same kernels, same order
+    on every buffer)."""
+    from context_attention_varlen_amd.ring import RankPlan, StepBuffers, rank_step
+    lens, cp, r, hq, hkv, d, mode, tf = _draw(seed)
+    print(f"seed {seed}: lens {lens} cp {cp} rank {r} heads {hq}/{hkv} d {d} mode {mode} tf {tf}", flush=True)
+    x, cu = _inputs(300 + seed, lens, hq, hkv, d, "bf16")
+    dq, dk, dv, delta, bufs = run_gpu(x, cu, cp, r, mode, "bf16", tf)
+    g = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    plan = RankPlan.make(cu, cp, r, tf=tf if tf[0] else None)
+    b = StepBuffers.make(plan, hq, hkv, d, torch.bfloat16, backward=True)
+    rank_step(g["q"], g["k"], g["v"], g["dout"], plan, mode, b, side=torch.cuda.Stream(), tf=tf)
+    torch.cuda.synchronize()
+    assert torch.equal(b.fwd.out, bufs.out) and torch.equal(b.fwd.lse, bufs.lse)
+    assert np.array_equal(b.dq.cpu().numpy(), dq) and np.array_equal(b.delta.cpu().numpy(), delta)
+    for j in range(cp):
+        assert np.array_equal(b.dk[j].cpu().numpy(), dk[j]) and np.array_equal(b.dv[j].cpu().numpy(), dv[j])
